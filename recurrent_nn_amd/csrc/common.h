@@ -1,0 +1,179 @@
+// common.h -- internal definitions shared by the host code and the kernels of
+// the MI355X ONNX RNN/GRU/LSTM library: the plan, the workspace layout and the
+// parameter blocks passed to the kernels.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/recurrent_nn_amd.h"
+
+namespace rnnamd {
+
+// Activation kinds (onemodel "Activations": the supported list).
+enum ActKind : int32_t {
+    ACT_SIGMOID = 0, ACT_TANH, ACT_RELU, ACT_AFFINE, ACT_LEAKYRELU,
+    ACT_THRESHOLDEDRELU, ACT_SCALEDTANH, ACT_HARDSIGMOID, ACT_ELU,
+    ACT_SOFTSIGN, ACT_SOFTPLUS, ACT_KIND_COUNT
+};
+
+struct ActSpec {
+    int32_t kind;
+    float alpha;
+    float beta;
+};
+
+// Stage indices for the optional event timing.
+enum Stage { STAGE_PACK = 0, STAGE_PROJ = 1, STAGE_REC = 2, STAGE_OTHER = 3, STAGE_COUNT = 4 };
+
+constexpr int kThreads = 256;          // threads per recurrence workgroup (4 waves)
+constexpr int kWaves = 4;
+constexpr int kMaxPairs = 8;           // (row, unit) pairs per thread in the epilogue
+constexpr int kMaxWorkgroups = 256;    // one workgroup per CU on MI355X
+
+// Workspace layout: byte offsets from the workspace base, each 256-aligned.
+struct Layout {
+    size_t wp = 0;      // packed W: rows in block-column order, [D*G*H][I] f32 or bf16
+    size_t rp = 0;      // packed R: [D][NUB][NT*16][Hp] f32, zero-padded
+    size_t xb = 0;      // X rounded to bf16 (bf16 projection only): [S*Bt][I]
+    size_t xw = 0;      // projections: [D][S][Bt][G*H] f32, block-column order
+    size_t hbuf = 0;    // H exchange, ping-pong: [2][D][Btp][Hp] f32
+    size_t sbuf = 0;    // GRU lbr=0: r (.) H_prev exchange [D][Btp][Hp]
+    size_t cbuf = 0;    // LSTM cell state between launches [D][Bt][H]
+    size_t zbuf = 0;    // GRU lbr=0 update gate between launches [D][Bt][H]
+    size_t lens = 0;    // int32 [Bt]
+    size_t bar = 0;     // uint32 barrier counters [D*NBB], then int32 error word
+    size_t total = 0;
+};
+
+}  // namespace rnnamd
+
+struct rnn_plan {
+    // operator
+    int32_t op = 0;           // rnn_op
+    int32_t G = 1;            // gates
+    int32_t D = 1;            // directions
+    int32_t reverse_only = 0;
+    int32_t layout = 0;
+    int32_t clip_on = 0;
+    float clip = 0.0f;
+    int32_t input_forget = 0;
+    int32_t lbr = 0;
+    int32_t proj_bf16 = 0;
+    int32_t constant_weights = 0;
+    int32_t kernel_path = 0;
+    int64_t S = 0, Bt = 0, I = 0, H = 0;
+    rnnamd::ActSpec act[2][3] = {};
+
+    // tiling of the recurrence
+    int32_t U = 1;            // hidden units per workgroup (last block may be ragged)
+    int32_t NUB = 1;          // unit blocks per direction
+    int32_t BT = 16;          // batch rows per workgroup (16, 32 or 64)
+    int32_t NBB = 1;          // batch blocks
+    int32_t MT = 1;           // 16-row MFMA tiles per workgroup (BT / 16)
+    int32_t NTA = 1;          // 16-column tiles of phase 0
+    int32_t NTB = 0;          // 16-column tiles of phase 1 (GRU lbr=0 candidate)
+    int32_t NT = 1;           // NTA + NTB
+    int32_t phases = 1;       // 2 for GRU lbr=0
+    int64_t Hp = 64;          // hidden padded to a multiple of 64 (K of the step product)
+    int32_t KB = 1;           // 16-wide k blocks per wave (Hp / 64)
+    int32_t resident = 0;     // R slice held in registers across steps
+    int64_t Btp = 16;         // NBB * BT
+    int32_t n_wg = 1;         // D * NBB * NUB
+
+    rnnamd::Layout ws;
+
+    // constant-weights cache: what the workspace holds packed
+    int32_t packed_valid = 0;
+    const void *packed_ws = nullptr;
+    const void *packed_W = nullptr, *packed_R = nullptr;
+
+    // device-dependent decisions, made on the first run
+    int32_t dev_ready = 0;
+    int32_t can_persist = 0;
+    int32_t device = -1;
+
+    // timing
+    int32_t timing = 0;
+    void *events[2 * rnnamd::STAGE_COUNT] = {};
+    int32_t events_recorded = 0;
+};
+
+namespace rnnamd {
+
+void set_error(const std::string &msg);
+int64_t round_up(int64_t x, int64_t m);
+void block_columns(const rnn_plan &p, int64_t ub, int32_t *u0, int32_t *uc);
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (defined in the .hip files).  Each returns a hipError_t
+// value as int (0 = success) and enqueues on `stream`.
+// ---------------------------------------------------------------------------
+
+struct PackArgs {
+    const float *W, *R;
+    void *Wp;           // f32 or bf16
+    float *Rp;
+    int64_t D, G, H, I, Hp;
+    int32_t U, NUB, NTA, NTB, phases, bf16;
+};
+int launch_pack(const PackArgs &a, void *stream);
+
+int launch_cast_bf16(const float *X, uint16_t *Xb, int64_t n, void *stream);
+
+struct InitArgs {
+    const float *h0, *c0;       // nullable, layout-dependent
+    float *hbuf, *sbuf, *cbuf;  // sbuf/cbuf nullable
+    int32_t *lens_dev;
+    int32_t fill_lens;          // >= 0: every row gets this length (sequence_lens absent)
+    uint32_t *bar;
+    int32_t n_bar;
+    int64_t D, Bt, Btp, H, Hp;
+    int32_t layout;
+};
+int launch_init(const InitArgs &a, void *stream);
+
+struct ProjArgs {
+    const void *X;          // f32 [M][I] or bf16
+    const void *Wp;         // f32 [N][I] or bf16
+    float *XW;              // [D][S][Bt][GH]
+    int64_t M, N, K;        // M = S*Bt, N = D*G*H, K = I
+    int64_t S, Bt, GH;
+    int32_t layout;         // row remap of layout 1
+    int32_t bf16;
+};
+int launch_projection(const ProjArgs &a, void *stream);
+
+struct RecArgs {
+    // sizes
+    int32_t S, Bt, H, D, G, op;
+    int32_t Hp, KB, U, NUB, BT, NBB, MT, NTA, NTB, NT, phases;
+    int32_t Btp;
+    int32_t reverse_only, layout, clip_on, input_forget, lbr;
+    float clip;
+    ActSpec act[2][3];
+    // buffers
+    const float *Rp, *XW, *B, *P;
+    const int32_t *lens;
+    float *hbuf, *sbuf, *cbuf, *zbuf;
+    float *Y, *Yh, *Yc;
+    uint32_t *bar;
+    int32_t *err;
+    uint32_t spin_limit;
+    // launch range in phase units (step j, phase p) -> q = j * phases + p
+    int32_t q_begin, q_end;
+};
+// persistent: one cooperative launch covering every phase; else one phase.
+int launch_recurrence(const RecArgs &a, int resident, int persistent, void *stream);
+int recurrence_can_persist(const RecArgs &a, int resident, int device, int *ok);
+bool recurrence_supported(int mt, int nt, int kb, int bt, int u, int resident);
+
+struct FinalArgs {
+    const float *h0, *c0;
+    float *Yh, *Yc;
+    int64_t n;              // D * Bt * H
+};
+int launch_zero_size_states(const FinalArgs &a, void *stream);
+
+}  // namespace rnnamd

@@ -1,0 +1,388 @@
+// plan.cpp -- host-side plan creation for the ONNX recurrent operators:
+// attribute parsing (activation names, defaults and alpha/beta cursors of the
+// onemodel page's "Activations" section), the checks of its "Choices the
+// specification leaves open" and "Limits" sections, the recurrence tiling and
+// the workspace layout.  Pure C++: no device call happens here, so every
+// plan-time error can be produced on a machine without a GPU.
+#include <algorithm>
+#include <cctype>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "common.h"
+
+namespace rnnamd {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string &msg) { g_last_error = msg; }
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Units [u0, u0 + uc) of unit block ub.
+void block_columns(const rnn_plan &p, int64_t ub, int32_t *u0, int32_t *uc)
+{
+    int64_t s = ub * p.U;
+    *u0 = (int32_t)s;
+    *uc = (int32_t)std::min<int64_t>(p.U, p.H - s);
+}
+
+namespace {
+
+struct NameKind {
+    const char *name;
+    int32_t kind;
+};
+const NameKind kNames[] = {
+    {"sigmoid", ACT_SIGMOID},       {"tanh", ACT_TANH},
+    {"relu", ACT_RELU},             {"affine", ACT_AFFINE},
+    {"leakyrelu", ACT_LEAKYRELU},   {"thresholdedrelu", ACT_THRESHOLDEDRELU},
+    {"scaledtanh", ACT_SCALEDTANH}, {"hardsigmoid", ACT_HARDSIGMOID},
+    {"elu", ACT_ELU},               {"softsign", ACT_SOFTSIGN},
+    {"softplus", ACT_SOFTPLUS},
+};
+
+int32_t kind_of(const char *name)
+{
+    if (!name)
+        return -1;
+    std::string low;
+    for (const char *c = name; *c; ++c)
+        low.push_back((char)std::tolower((unsigned char)*c));
+    for (const auto &nk : kNames)
+        if (low == nk.name)
+            return nk.kind;
+    return -1;
+}
+
+bool uses_alpha(int32_t k)
+{
+    return k == ACT_AFFINE || k == ACT_SCALEDTANH || k == ACT_HARDSIGMOID ||
+           k == ACT_LEAKYRELU || k == ACT_THRESHOLDEDRELU || k == ACT_ELU;
+}
+bool uses_beta(int32_t k) { return k == ACT_AFFINE || k == ACT_SCALEDTANH || k == ACT_HARDSIGMOID; }
+
+float alpha_default(int32_t k)
+{
+    switch (k) {
+    case ACT_LEAKYRELU: return 0.01f;
+    case ACT_HARDSIGMOID: return 0.2f;
+    case ACT_THRESHOLDEDRELU:
+    case ACT_ELU:
+    case ACT_AFFINE:
+    case ACT_SCALEDTANH: return 1.0f;
+    default: return 0.0f;
+    }
+}
+float beta_default(int32_t k) { return k == ACT_HARDSIGMOID ? 0.5f : 0.0f; }
+
+rnn_status resolve_activations(const rnn_attrs &a, rnn_plan &p)
+{
+    const int na = p.op == RNN_OP_LSTM ? 3 : p.op == RNN_OP_GRU ? 2 : 1;
+    static const int32_t defaults[3][3] = {{ACT_TANH, 0, 0},
+                                           {ACT_SIGMOID, ACT_TANH, 0},
+                                           {ACT_SIGMOID, ACT_TANH, ACT_TANH}};
+    if (a.n_activations == 0 || a.activations == nullptr) {
+        for (int d = 0; d < p.D; ++d)
+            for (int j = 0; j < na; ++j) {
+                int32_t k = defaults[p.op][j];
+                p.act[d][j] = {k, alpha_default(k), beta_default(k)};
+            }
+        return RNN_OK;
+    }
+    if (!(a.n_activations == na || (p.D == 2 && a.n_activations == 2 * na))) {
+        set_error("activations: expected " + std::to_string(na) + " names per direction set, got " +
+                  std::to_string(a.n_activations));
+        return RNN_ERR_INVALID_INPUT;
+    }
+    ActSpec list[6];
+    int ca = 0, cb = 0;
+    for (int i = 0; i < a.n_activations; ++i) {
+        int32_t k = kind_of(a.activations[i]);
+        if (k < 0) {
+            set_error(std::string("activations: unknown name '") +
+                      (a.activations[i] ? a.activations[i] : "(null)") + "'");
+            return RNN_ERR_INVALID_INPUT;
+        }
+        ActSpec s{k, alpha_default(k), beta_default(k)};
+        // separate cursors for alpha and beta, walked in activation order
+        if (uses_alpha(k) && ca < a.n_alpha && a.activation_alpha)
+            s.alpha = a.activation_alpha[ca++];
+        if (uses_beta(k) && cb < a.n_beta && a.activation_beta)
+            s.beta = a.activation_beta[cb++];
+        list[i] = s;
+    }
+    for (int d = 0; d < p.D; ++d)
+        for (int j = 0; j < na; ++j)
+            p.act[d][j] = (a.n_activations == na) ? list[j] : list[d * na + j];
+    return RNN_OK;
+}
+
+// Column tiles of one unit block for a unit count uc.
+void tiles_for(const rnn_plan &p, int uc, int *nta, int *ntb)
+{
+    if (p.op == RNN_OP_GRU && !p.lbr) {
+        *nta = (2 * uc + 15) / 16;
+        *ntb = (uc + 15) / 16;
+    } else {
+        *nta = (p.G * uc + 15) / 16;
+        *ntb = 0;
+    }
+}
+
+// The recurrence kernel is compiled for these shapes only (recurrence.hip).
+// R in registers: 2 or 4 row tiles, 1 or 2 column tiles, 8 or 16 k blocks of
+// 16 per wave, at most 2 (row, unit) pairs per thread.
+bool resident_ok(int nt, int kb, int mt, int pairs)
+{
+    return (mt == 2 || mt == 4) && nt <= 2 && (kb == 8 || kb == 16) && pairs <= 2;
+}
+
+// R streamed every step: 1, 2, 4 or 6 column tiles, at most 8 pairs.
+bool streamed_ok(int nt, int pairs)
+{
+    return (nt == 1 || nt == 2 || nt == 4 || nt == 6) && pairs <= kMaxPairs;
+}
+
+// Choose units per workgroup: at most kMaxWorkgroups workgroups, the least
+// matrix-core work per wave per step, then the fewest workgroups.
+rnn_status choose_tiling(const rnn_attrs &a, rnn_plan &p)
+{
+    if (a.batch_tile) {
+        if (a.batch_tile != 16 && a.batch_tile != 32 && a.batch_tile != 64) {
+            set_error("batch_tile must be 0, 16, 32 or 64");
+            return RNN_ERR_INVALID_INPUT;
+        }
+        p.BT = a.batch_tile;
+    } else {
+        p.BT = p.Bt <= 16 ? 16 : p.Bt <= 32 ? 32 : 64;
+    }
+    p.MT = p.BT / 16;
+    p.NBB = (int32_t)std::max<int64_t>(1, (p.Bt + p.BT - 1) / p.BT);
+    p.Btp = (int64_t)p.NBB * p.BT;
+    p.Hp = round_up(std::max<int64_t>(p.H, 1), 64);
+    p.KB = (int32_t)(p.Hp / 64);
+    p.phases = (p.op == RNN_OP_GRU && !p.lbr) ? 2 : 1;
+
+    bool cap_wg = true;   // first look for tilings whose workgroups fit at once
+    auto evaluate = [&](int u, int *nta, int *ntb, bool *res, long *cost) -> bool {
+        int nub = (int)((p.H + u - 1) / u);
+        long wg = (long)p.D * p.NBB * nub;
+        if (cap_wg && wg > kMaxWorkgroups && !a.units_per_block)
+            return false;
+        if ((long)p.BT * u > (long)kThreads * kMaxPairs)
+            return false;
+        tiles_for(p, u, nta, ntb);
+        int nt = *nta + *ntb;
+        int pairs = (p.BT * u + kThreads - 1) / kThreads;
+        *res = resident_ok(nt, p.KB, p.MT, pairs);
+        if (!*res && !streamed_ok(nt, pairs))
+            return false;
+        long lds = ((long)kWaves * p.BT * (nt * 16 + 4) + 3L * p.BT * u + p.BT) * 4;
+        if (lds > 160 * 1024)
+            return false;
+        *cost = (long)p.MT * nt * p.KB * 16 + (*res ? 0 : (long)p.MT * nt * p.KB * 4);
+        return true;
+    };
+
+    int best_u = -1, bnta = 0, bntb = 0;
+    bool bres = false;
+    long bcost = 0;
+    if (a.units_per_block) {
+        int u = a.units_per_block;
+        if (u < 1 || u > p.H) {
+            set_error("units_per_block out of range");
+            return RNN_ERR_INVALID_INPUT;
+        }
+        long c;
+        bool r;
+        if (!evaluate(u, &bnta, &bntb, &r, &c)) {
+            set_error("units_per_block gives an unsupported tiling");
+            return RNN_ERR_INVALID_INPUT;
+        }
+        best_u = u;
+        bres = r;
+    } else {
+        for (int pass = 0; pass < 2 && best_u < 0; ++pass) {
+            cap_wg = pass == 0;   // second pass: more workgroups, run one step per launch
+            for (int u = 1; u <= std::min<int64_t>(p.H, 128); ++u) {
+                int nta, ntb;
+                bool r;
+                long c;
+                if (!evaluate(u, &nta, &ntb, &r, &c))
+                    continue;
+                if (best_u < 0 || c < bcost || (c == bcost && u > best_u)) {
+                    best_u = u;
+                    bcost = c;
+                    bnta = nta;
+                    bntb = ntb;
+                    bres = r;
+                }
+            }
+        }
+        if (best_u < 0) {
+            set_error("no recurrence tiling fits this shape");
+            return RNN_ERR_UNSUPPORTED;
+        }
+    }
+    p.U = best_u;
+    p.NUB = (int32_t)((p.H + p.U - 1) / p.U);
+    p.NTA = bnta;
+    p.NTB = bntb;
+    p.NT = bnta + bntb;
+    p.resident = bres ? 1 : 0;
+    p.n_wg = p.D * p.NBB * p.NUB;
+    return RNN_OK;
+}
+
+void make_layout(rnn_plan &p)
+{
+    Layout &L = p.ws;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += (size_t)round_up((int64_t)bytes, 256);
+        return o;
+    };
+    const size_t GH = (size_t)p.G * p.H;
+    const size_t wsz = p.proj_bf16 ? 2 : 4;
+    L.wp = take((size_t)p.D * GH * p.I * wsz);
+    L.rp = take((size_t)p.D * p.NUB * p.NT * 16 * p.Hp * 4);
+    L.xb = take(0);   // X is rounded to bf16 inside the projection's staging
+    L.xw = take((size_t)p.D * p.S * p.Bt * GH * 4);
+    L.hbuf = take((size_t)2 * p.D * p.Btp * p.Hp * 4);
+    L.sbuf = take(p.phases == 2 ? (size_t)p.D * p.Btp * p.Hp * 4 : 0);
+    L.cbuf = take(p.op == RNN_OP_LSTM ? (size_t)p.D * p.Bt * p.H * 4 : 0);
+    L.zbuf = take(p.phases == 2 ? (size_t)p.D * p.Bt * p.H * 4 : 0);
+    L.lens = take((size_t)std::max<int64_t>(p.Bt, 1) * 4);
+    L.bar = take((size_t)(p.D * p.NBB + 1) * 4);
+    L.total = off;
+}
+
+}  // namespace
+}  // namespace rnnamd
+
+using namespace rnnamd;
+
+extern "C" const char *rnn_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" rnn_status rnn_plan_create(const rnn_attrs *attrs, const rnn_dims *dims, rnn_plan **out)
+{
+    set_error("");
+    if (!attrs || !dims || !out) {
+        set_error("rnn_plan_create: NULL argument");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    *out = nullptr;
+    const rnn_attrs &a = *attrs;
+    rnn_plan *p = new (std::nothrow) rnn_plan();
+    if (!p) {
+        set_error("rnn_plan_create: out of host memory");
+        return RNN_ERR_OUT_OF_MEMORY;
+    }
+    auto fail = [&](rnn_status s, const std::string &m) {
+        if (!m.empty())
+            set_error(m);
+        delete p;
+        return s;
+    };
+    if (a.op != RNN_OP_RNN && a.op != RNN_OP_GRU && a.op != RNN_OP_LSTM)
+        return fail(RNN_ERR_INVALID_INPUT, "unknown op");
+    p->op = a.op;
+    p->G = a.op == RNN_OP_LSTM ? 4 : a.op == RNN_OP_GRU ? 3 : 1;
+    int want_d = 1;
+    if (a.direction == nullptr || std::strcmp(a.direction, "forward") == 0) {
+        want_d = 1;
+    } else if (std::strcmp(a.direction, "reverse") == 0) {
+        want_d = 1;
+        p->reverse_only = 1;
+    } else if (std::strcmp(a.direction, "bidirectional") == 0) {
+        want_d = 2;
+    } else {
+        return fail(RNN_ERR_INVALID_INPUT, "direction must be forward, reverse or bidirectional");
+    }
+    if (dims->num_directions != want_d)
+        return fail(RNN_ERR_INVALID_INPUT, "num_directions does not match direction");
+    p->D = want_d;
+    if (a.layout != 0 && a.layout != 1)
+        return fail(RNN_ERR_INVALID_INPUT, "layout must be 0 or 1");
+    p->layout = a.layout;
+    if (dims->seq_length < 0 || dims->batch_size < 0 || dims->input_size < 0 || dims->hidden < 0)
+        return fail(RNN_ERR_INVALID_INPUT, "negative dimension");
+    if (dims->hidden == 0)
+        return fail(RNN_ERR_INVALID_INPUT, "hidden size is zero");
+    if (a.hidden_size != 0 && a.hidden_size != dims->hidden)
+        return fail(RNN_ERR_INVALID_INPUT, "hidden_size does not match R's last dimension");
+    if (a.op != RNN_OP_LSTM && a.input_forget)
+        return fail(RNN_ERR_INVALID_INPUT, "input_forget is an LSTM attribute");
+    if (a.op != RNN_OP_GRU && a.linear_before_reset)
+        return fail(RNN_ERR_INVALID_INPUT, "linear_before_reset is a GRU attribute");
+    if (a.proj_dtype != RNN_PROJ_F32 && a.proj_dtype != RNN_PROJ_BF16)
+        return fail(RNN_ERR_INVALID_INPUT, "proj_dtype must be F32 or BF16");
+    if (a.kernel_path < RNN_PATH_AUTO || a.kernel_path > RNN_PATH_PER_STEP)
+        return fail(RNN_ERR_INVALID_INPUT, "unknown kernel_path");
+    p->S = dims->seq_length;
+    p->Bt = dims->batch_size;
+    p->I = dims->input_size;
+    p->H = dims->hidden;
+    p->clip_on = (a.has_clip && a.clip > 0.0f) ? 1 : 0;   // "when present and positive"
+    p->clip = a.clip;
+    p->input_forget = a.input_forget ? 1 : 0;
+    p->lbr = a.linear_before_reset ? 1 : 0;
+    p->proj_bf16 = a.proj_dtype == RNN_PROJ_BF16;
+    p->constant_weights = a.constant_weights ? 1 : 0;
+    p->kernel_path = a.kernel_path;
+
+    rnn_status st = resolve_activations(a, *p);
+    if (st != RNN_OK)
+        return fail(st, "");
+
+    // Limits: per direction, seq*batch*G*H + 4*batch*H (+ transposed weights
+    // when not constant) floats must stay below 2^30.
+    double need = (double)p->S * (double)p->Bt * p->G * (double)p->H + 4.0 * (double)p->Bt * p->H;
+    if (!p->constant_weights)
+        need += (double)p->G * p->H * ((double)p->I + (double)p->H);
+    if (!(need < 1073741824.0))
+        return fail(RNN_ERR_UNSUPPORTED, "per-direction scratch reaches 2^30 floats");
+    if (p->H > 65536 || p->I > (int64_t)1 << 30 || p->S > INT32_MAX || p->Bt > INT32_MAX)
+        return fail(RNN_ERR_UNSUPPORTED, "dimension beyond this library's index range");
+
+    if (p->S > 0 && p->Bt > 0) {
+        st = choose_tiling(a, *p);
+        if (st != RNN_OK)
+            return fail(st, "");
+        make_layout(*p);
+    }
+    *out = p;
+    return RNN_OK;
+}
+
+extern "C" rnn_status rnn_plan_workspace_size(const rnn_plan *plan, size_t *bytes)
+{
+    if (!plan || !bytes) {
+        set_error("rnn_plan_workspace_size: NULL argument");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    *bytes = (plan->S > 0 && plan->Bt > 0) ? plan->ws.total : 0;
+    return RNN_OK;
+}
+
+extern "C" rnn_status rnn_plan_describe(const rnn_plan *p, char *buf, size_t len)
+{
+    if (!p || !buf || len == 0) {
+        set_error("rnn_plan_describe: NULL argument");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    std::snprintf(buf, len,
+                  "op=%d G=%d D=%d S=%lld Bt=%lld I=%lld H=%lld U=%d NUB=%d BT=%d NBB=%d MT=%d "
+                  "NTA=%d NTB=%d phases=%d Hp=%lld KB=%d resident=%d workgroups=%d path=%d "
+                  "persist=%d ws=%zu",
+                  p->op, p->G, p->D, (long long)p->S, (long long)p->Bt, (long long)p->I,
+                  (long long)p->H, p->U, p->NUB, p->BT, p->NBB, p->MT, p->NTA, p->NTB, p->phases,
+                  (long long)p->Hp, p->KB, p->resident, p->n_wg, p->kernel_path, p->can_persist,
+                  p->ws.total);
+    return RNN_OK;
+}

@@ -1,0 +1,256 @@
+// proj_gemm.hip -- the input projection XW = X . W^T over all time steps
+// (onemodel "Recurrent operators", section "Computation", step 1: one matrix
+// product of shape [seq*batch, G*H] per direction).  Both directions are one
+// product with N = dirs*G*H; W arrives packed (rows in block-column order,
+// see pack.hip), so XW comes out in the order the recurrence reads it.
+//
+// Tiling: 128x128 output tile per 256-thread workgroup, 4 waves of 64x64, K
+// staged through LDS in 128-byte row slices (32 fp32 or 64 bf16 values) with
+// double buffering.  fp32 uses v_mfma_f32_16x16x4_f32, bf16 uses the gfx950
+// v_mfma_f32_16x16x32_bf16; for bf16, X is rounded to bfloat16 (nearest even)
+// while it is staged, so no separate cast pass runs.  Accumulation is in the
+// matrix cores' order with a fixed tiling (deterministic, "fast mode").
+//
+// Each lane feeds the matrix core 16 contiguous bytes of one row per 16x16
+// tile and k block: lane (r = l % 16, q = l / 16) supplies k = 4q..4q+3 (fp32)
+// or 8q..8q+7 (bf16) of the block; for fp32 the four components go to four
+// consecutive MFMAs, i.e. the k order inside a block is permuted, which only
+// changes the (already unspecified) summation order.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace rnnamd {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 128, BN = 128;
+constexpr int ROWB = 128;              // bytes of k per row per stage
+constexpr int LDSROW = ROWB + 16;      // padded LDS row stride (bytes)
+constexpr int TILEB = BM * LDSROW;     // bytes of one operand tile in LDS
+
+__device__ __forceinline__ uint32_t bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+        return (u >> 16) | 0x0040u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// 4 fp32 values of row `row` at k .. k+3, zero outside [0, rows) x [0, K).
+__device__ __forceinline__ f4 load4(const float *__restrict__ p, int64_t row, int64_t k,
+                                    int64_t rows, int64_t K, bool vec_ok)
+{
+    f4 v = {0.f, 0.f, 0.f, 0.f};
+    if (row >= rows)
+        return v;
+    const float *q = p + row * K + k;
+    if (vec_ok && k + 3 < K)
+        return *(const f4 *)q;
+    if (k + 0 < K) v[0] = q[0];
+    if (k + 1 < K) v[1] = q[1];
+    if (k + 2 < K) v[2] = q[2];
+    if (k + 3 < K) v[3] = q[3];
+    return v;
+}
+
+// 8 bf16 values (16 bytes) of row `row` at k .. k+7 of a bf16 matrix.
+__device__ __forceinline__ u4 load8h(const uint16_t *__restrict__ p, int64_t row, int64_t k,
+                                     int64_t rows, int64_t K, bool vec_ok)
+{
+    u4 v = {0u, 0u, 0u, 0u};
+    if (row >= rows)
+        return v;
+    const uint16_t *q = p + row * K + k;
+    if (vec_ok && k + 7 < K)
+        return *(const u4 *)q;
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        h[e] = (k + e < K) ? q[e] : 0u;
+    v[0] = h[0] | (h[1] << 16);
+    v[1] = h[2] | (h[3] << 16);
+    v[2] = h[4] | (h[5] << 16);
+    v[3] = h[6] | (h[7] << 16);
+    return v;
+}
+
+__device__ __forceinline__ u4 pack8(f4 a, f4 b)
+{
+    u4 v;
+    v[0] = bf16_bits(a[0]) | (bf16_bits(a[1]) << 16);
+    v[1] = bf16_bits(a[2]) | (bf16_bits(a[3]) << 16);
+    v[2] = bf16_bits(b[0]) | (bf16_bits(b[1]) << 16);
+    v[3] = bf16_bits(b[2]) | (bf16_bits(b[3]) << 16);
+    return v;
+}
+
+// Tile order: workgroups on one XCD (blockIdx % 8) take a contiguous range
+// of tiles, walked in bands of GM tile-rows so that neighbours share panels.
+__device__ __forceinline__ void tile_of(int64_t wg, int64_t nwg, int64_t tiles_m, int64_t tiles_n,
+                                        int64_t *tm, int64_t *tn)
+{
+    int64_t t = wg;
+    if (nwg % 8 == 0)
+        t = (wg % 8) * (nwg / 8) + wg / 8;
+    constexpr int64_t GM = 8;
+    const int64_t band = GM * tiles_n;
+    const int64_t g = t / band;
+    const int64_t first = g * GM;
+    const int64_t gm = (tiles_m - first) < GM ? (tiles_m - first) : GM;
+    const int64_t r = t - g * band;
+    *tm = first + r % gm;
+    *tn = r / gm;
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];   // [2][A,B][TILEB]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
+    const int wm = w >> 1, wn = w & 1;
+
+    const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+    int64_t tm, tn;
+    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+
+    // k values per stage: 32 (fp32) or 64 (bf16)
+    constexpr int KS = BF16 ? 64 : 32;
+    const int64_t nk = (a.K + KS - 1) / KS;
+    const bool a_vec = BF16 ? (a.K % 4 == 0) : (a.K % 4 == 0);
+    const bool b_vec = BF16 ? (a.K % 8 == 0) : (a.K % 4 == 0);
+
+    // staging: thread -> (row = tid / 8 + 32 i, chunk = tid % 8 of 16 bytes)
+    const int srow = tid >> 3, sch = tid & 7;
+    u4 ra[4], rb[4];
+    auto gload = [&](int64_t kt) {
+        const int64_t kbase = kt * KS;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t row = srow + 32 * i;
+            if constexpr (BF16) {
+                const float *X = (const float *)a.X;
+                const int64_t k = kbase + sch * 8;
+                f4 x0 = load4(X, m0 + row, k, a.M, a.K, a_vec);
+                f4 x1 = load4(X, m0 + row, k + 4, a.M, a.K, a_vec);
+                ra[i] = pack8(x0, x1);
+                rb[i] = load8h((const uint16_t *)a.Wp, n0 + row, k, a.N, a.K, b_vec);
+            } else {
+                const int64_t k = kbase + sch * 4;
+                f4 x = load4((const float *)a.X, m0 + row, k, a.M, a.K, a_vec);
+                f4 y = load4((const float *)a.Wp, n0 + row, k, a.N, a.K, b_vec);
+                ra[i] = __builtin_bit_cast(u4, x);
+                rb[i] = __builtin_bit_cast(u4, y);
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+        unsigned char *A = lds + buf * 2 * TILEB;
+        unsigned char *B = A + TILEB;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = srow + 32 * i;
+            *(u4 *)(A + row * LDSROW + sch * 16) = ra[i];
+            *(u4 *)(B + row * LDSROW + sch * 16) = rb[i];
+        }
+    };
+
+    f4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int buf = (int)(kt & 1);
+        if (kt + 1 < nk)
+            gload(kt + 1);
+        const unsigned char *A = lds + buf * 2 * TILEB;
+        const unsigned char *B = A + TILEB;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {            // two 64-byte k blocks per stage
+            u4 av[4], bv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                av[i] = *(const u4 *)(A + (wm * 64 + i * 16 + lr) * LDSROW + kb * 64 + lq * 16);
+                bv[i] = *(const u4 *)(B + (wn * 64 + i * 16 + lr) * LDSROW + kb * 64 + lq * 16);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if constexpr (BF16) {
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf8, av[i]), __builtin_bit_cast(bf8, bv[j]),
+                            acc[i][j], 0, 0, 0);
+                    } else {
+                        const f4 x = __builtin_bit_cast(f4, av[i]);
+                        const f4 y = __builtin_bit_cast(f4, bv[j]);
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], y[s], acc[i][j],
+                                                                             0, 0, 0);
+                    }
+                }
+        }
+        if (kt + 1 < nk)
+            sstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // store: lane holds rows 4*lq + r, column lr of each 16x16 tile
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t m = m0 + wm * 64 + i * 16 + lq * 4 + r;
+            if (m >= a.M)
+                continue;
+            int64_t xrow;   // row of XW[d] = t * Bt + b
+            if (a.layout == 0) {
+                xrow = m;
+            } else {
+                const int64_t b = m / a.S, t = m - b * a.S;
+                xrow = t * a.Bt + b;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t n = n0 + wn * 64 + j * 16 + lr;
+                if (n >= a.N)
+                    continue;
+                const int64_t d = n / a.GH, nl = n - d * a.GH;
+                a.XW[(d * a.S * a.Bt + xrow) * a.GH + nl] = acc[i][j][r];
+            }
+        }
+}
+
+int launch_projection(const ProjArgs &a, void *stream)
+{
+    if (a.M <= 0 || a.N <= 0)
+        return 0;
+    const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    const size_t shmem = 2 * 2 * TILEB;
+    const void *fn = a.bf16 ? (const void *)proj_gemm_kernel<true> : (const void *)proj_gemm_kernel<false>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess)
+        return (int)e;
+    if (a.bf16)
+        hipLaunchKernelGGL(proj_gemm_kernel<true>, dim3((unsigned)tiles), dim3(256), shmem,
+                           (hipStream_t)stream, a);
+    else
+        hipLaunchKernelGGL(proj_gemm_kernel<false>, dim3((unsigned)tiles), dim3(256), shmem,
+                           (hipStream_t)stream, a);
+    return (int)hipGetLastError();
+}
+
+}  // namespace rnnamd

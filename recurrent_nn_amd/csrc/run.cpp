@@ -1,0 +1,365 @@
+// run.cpp -- rnn_run: host-side checks (every one before anything is
+// enqueued), then the stream-ordered launch sequence
+//   pack W and R (unless constant and already packed)  -> init states
+//   -> projection XW = X . W^T over all steps -> step loop -> (final states
+//   are written by the step loop itself)
+// for the ONNX recurrent operators.  The sequence_lens range check is the
+// onemodel page's run-time InvalidInput ("Choices the specification leaves
+// open"); seq = 0 or batch = 0 runs nothing but the initial-state copy.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "common.h"
+
+using namespace rnnamd;
+
+namespace {
+
+constexpr uint32_t kSpinLimit = 1u << 26;   // ~seconds of s_sleep: a barrier takes microseconds
+
+rnn_status hip_fail(hipError_t e, const char *where)
+{
+    set_error(std::string(where) + ": " + hipGetErrorString(e));
+    return RNN_ERR_DEVICE;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Timer {
+    rnn_plan *p;
+    hipStream_t s;
+    void begin(int stage)
+    {
+        if (p->timing)
+            (void)hipEventRecord((hipEvent_t)p->events[2 * stage], s);
+    }
+    void end(int stage)
+    {
+        if (p->timing)
+            (void)hipEventRecord((hipEvent_t)p->events[2 * stage + 1], s);
+    }
+};
+
+RecArgs rec_args(const rnn_plan &p, unsigned char *ws, const float *B, const float *P, float *Y,
+                 float *Yh, float *Yc)
+{
+    RecArgs r{};
+    r.S = (int32_t)p.S;
+    r.Bt = (int32_t)p.Bt;
+    r.H = (int32_t)p.H;
+    r.D = p.D;
+    r.G = p.G;
+    r.op = p.op;
+    r.Hp = (int32_t)p.Hp;
+    r.KB = p.KB;
+    r.U = p.U;
+    r.NUB = p.NUB;
+    r.BT = p.BT;
+    r.NBB = p.NBB;
+    r.MT = p.MT;
+    r.NTA = p.NTA;
+    r.NTB = p.NTB;
+    r.NT = p.NT;
+    r.phases = p.phases;
+    r.Btp = (int32_t)p.Btp;
+    r.reverse_only = p.reverse_only;
+    r.layout = p.layout;
+    r.clip_on = p.clip_on;
+    r.clip = p.clip;
+    r.input_forget = p.input_forget;
+    r.lbr = p.lbr;
+    std::memcpy(r.act, p.act, sizeof(r.act));
+    r.Rp = (const float *)(ws + p.ws.rp);
+    r.XW = (const float *)(ws + p.ws.xw);
+    r.B = B;
+    r.P = P;
+    r.lens = (const int32_t *)(ws + p.ws.lens);
+    r.hbuf = (float *)(ws + p.ws.hbuf);
+    r.sbuf = p.phases == 2 ? (float *)(ws + p.ws.sbuf) : nullptr;
+    r.cbuf = p.op == RNN_OP_LSTM ? (float *)(ws + p.ws.cbuf) : nullptr;
+    r.zbuf = p.phases == 2 ? (float *)(ws + p.ws.zbuf) : nullptr;
+    r.Y = Y;
+    r.Yh = Yh;
+    r.Yc = Yc;
+    r.bar = (uint32_t *)(ws + p.ws.bar);
+    r.err = (int32_t *)(ws + p.ws.bar) + p.D * p.NBB;
+    r.spin_limit = kSpinLimit;
+    r.q_begin = 0;
+    r.q_end = (int32_t)(p.S * p.phases);
+    return r;
+}
+
+rnn_status device_setup(rnn_plan *p, unsigned char *ws)
+{
+    if (p->dev_ready)
+        return RNN_OK;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    p->device = dev;
+    RecArgs r = rec_args(*p, ws, nullptr, nullptr, nullptr, nullptr, nullptr);
+    int ok = 0;
+    int rc = recurrence_can_persist(r, p->resident, dev, &ok);
+    if (rc != 0)
+        return hip_fail((hipError_t)rc, "recurrence occupancy query");
+    p->can_persist = ok;
+    if (p->kernel_path == RNN_PATH_PERSISTENT && !ok) {
+        set_error("persistent path requested but the workgroups cannot all be resident");
+        return RNN_ERR_UNSUPPORTED;
+    }
+    if (p->timing) {
+        for (int i = 0; i < 2 * STAGE_COUNT; ++i)
+            if (!p->events[i]) {
+                hipEvent_t ev;
+                e = hipEventCreate(&ev);
+                if (e != hipSuccess)
+                    return hip_fail(e, "hipEventCreate");
+                p->events[i] = ev;
+            }
+    }
+    p->dev_ready = 1;
+    return RNN_OK;
+}
+
+}  // namespace
+
+extern "C" rnn_status rnn_run(rnn_plan *p, void *hip_stream, void *workspace, size_t workspace_bytes,
+                              const float *X, const float *W, const float *R, const float *B,
+                              const int32_t *sequence_lens, const float *initial_h,
+                              const float *initial_c, const float *P, float *Y, float *Y_h,
+                              float *Y_c)
+{
+    set_error("");
+    if (!p) {
+        set_error("rnn_run: NULL plan");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    hipStream_t s = (hipStream_t)hip_stream;
+    const bool zero = p->S == 0 || p->Bt == 0;
+    if (p->op != RNN_OP_LSTM && (initial_c || P || Y_c)) {
+        set_error("rnn_run: initial_c, P and Y_c are LSTM-only");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    if (!zero && (!X || !W || !R)) {
+        set_error("rnn_run: X, W and R are required");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    const void *ptrs[] = {X, W, R, B, initial_h, initial_c, P, Y, Y_h, Y_c};
+    for (const void *q : ptrs)
+        if (q && !aligned(q, 4)) {
+            set_error("rnn_run: tensors must be 4-byte aligned");
+            return RNN_ERR_INVALID_INPUT;
+        }
+    if (X && !aligned(X, 16)) {
+        set_error("rnn_run: X must be 16-byte aligned");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    if (sequence_lens)
+        for (int64_t b = 0; b < p->Bt; ++b)
+            if (sequence_lens[b] < 0 || sequence_lens[b] > p->S) {
+                set_error("rnn_run: sequence_lens[" + std::to_string(b) + "] = " +
+                          std::to_string(sequence_lens[b]) + " is outside [0, seq]");
+                return RNN_ERR_INVALID_INPUT;
+            }
+
+    if (zero) {
+        FinalArgs f{initial_h, initial_c, Y_h, Y_c, (int64_t)p->D * p->Bt * p->H};
+        int rc = launch_zero_size_states(f, s);
+        return rc ? hip_fail((hipError_t)rc, "zero-size state copy") : RNN_OK;
+    }
+
+    if (!workspace || workspace_bytes < p->ws.total || !aligned(workspace, 256)) {
+        set_error("rnn_run: workspace missing, smaller than rnn_plan_workspace_size() or not "
+                  "256-byte aligned");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    unsigned char *ws = (unsigned char *)workspace;
+    rnn_status st = device_setup(p, ws);
+    if (st != RNN_OK)
+        return st;
+    const bool persistent = p->kernel_path == RNN_PATH_PERSISTENT ||
+                            (p->kernel_path == RNN_PATH_AUTO && p->can_persist);
+    Timer tm{p, s};
+    p->events_recorded = p->timing;
+    hipError_t e;
+
+    // 1. pack W (block-column row order, optional bf16) and R (padded tiles)
+    tm.begin(STAGE_PACK);
+    const bool reuse = p->constant_weights && p->packed_valid && p->packed_ws == workspace &&
+                       p->packed_W == W && p->packed_R == R;
+    if (!reuse) {
+        PackArgs pa{};
+        pa.W = W;
+        pa.R = R;
+        pa.Wp = ws + p->ws.wp;
+        pa.Rp = (float *)(ws + p->ws.rp);
+        pa.D = p->D;
+        pa.G = p->G;
+        pa.H = p->H;
+        pa.I = p->I;
+        pa.Hp = p->Hp;
+        pa.U = p->U;
+        pa.NUB = p->NUB;
+        pa.NTA = p->NTA;
+        pa.NTB = p->NTB;
+        pa.phases = p->phases;
+        pa.bf16 = p->proj_bf16;
+        int rc = launch_pack(pa, s);
+        if (rc)
+            return hip_fail((hipError_t)rc, "weight pack");
+        p->packed_valid = p->constant_weights;
+        p->packed_ws = workspace;
+        p->packed_W = W;
+        p->packed_R = R;
+    }
+    tm.end(STAGE_PACK);
+
+    // 2. states, exchange buffers, barrier counters, lengths
+    tm.begin(STAGE_OTHER);
+    int32_t *lens_dev = (int32_t *)(ws + p->ws.lens);
+    if (sequence_lens) {
+        e = hipMemcpyAsync(lens_dev, sequence_lens, (size_t)p->Bt * sizeof(int32_t),
+                           hipMemcpyHostToDevice, s);
+        if (e != hipSuccess)
+            return hip_fail(e, "sequence_lens copy");
+    }
+    InitArgs ia{};
+    ia.h0 = initial_h;
+    ia.c0 = p->op == RNN_OP_LSTM ? initial_c : nullptr;
+    ia.hbuf = (float *)(ws + p->ws.hbuf);
+    ia.sbuf = p->phases == 2 ? (float *)(ws + p->ws.sbuf) : nullptr;
+    ia.cbuf = p->op == RNN_OP_LSTM ? (float *)(ws + p->ws.cbuf) : nullptr;
+    ia.lens_dev = lens_dev;
+    ia.fill_lens = sequence_lens ? -1 : (int32_t)p->S;
+    ia.bar = (uint32_t *)(ws + p->ws.bar);
+    ia.n_bar = p->D * p->NBB;
+    ia.D = p->D;
+    ia.Bt = p->Bt;
+    ia.Btp = p->Btp;
+    ia.H = p->H;
+    ia.Hp = p->Hp;
+    ia.layout = p->layout;
+    int rc = launch_init(ia, s);
+    if (rc)
+        return hip_fail((hipError_t)rc, "state init");
+    tm.end(STAGE_OTHER);
+
+    // 3. projection of all steps, both directions in one product
+    tm.begin(STAGE_PROJ);
+    ProjArgs pr{};
+    pr.X = X;
+    pr.Wp = ws + p->ws.wp;
+    pr.XW = (float *)(ws + p->ws.xw);
+    pr.M = p->S * p->Bt;
+    pr.N = (int64_t)p->D * p->G * p->H;
+    pr.K = p->I;
+    pr.S = p->S;
+    pr.Bt = p->Bt;
+    pr.GH = (int64_t)p->G * p->H;
+    pr.layout = p->layout;
+    pr.bf16 = p->proj_bf16;
+    rc = launch_projection(pr, s);
+    if (rc)
+        return hip_fail((hipError_t)rc, "projection");
+    tm.end(STAGE_PROJ);
+
+    // 4. the step loop
+    tm.begin(STAGE_REC);
+    RecArgs ra = rec_args(*p, ws, B, P, Y, Y_h, Y_c);
+    if (persistent) {
+        rc = launch_recurrence(ra, p->resident, 1, s);
+        if (rc)
+            return hip_fail((hipError_t)rc, "recurrence (persistent)");
+    } else {
+        const int32_t nq = (int32_t)(p->S * p->phases);
+        for (int32_t q = 0; q < nq; ++q) {
+            ra.q_begin = q;
+            ra.q_end = q + 1;
+            rc = launch_recurrence(ra, p->resident, 0, s);
+            if (rc)
+                return hip_fail((hipError_t)rc, "recurrence (per step)");
+        }
+    }
+    tm.end(STAGE_REC);
+    return RNN_OK;
+}
+
+extern "C" rnn_status rnn_workspace_check(const rnn_plan *p, void *hip_stream, const void *workspace)
+{
+    if (!p || !workspace) {
+        set_error("rnn_workspace_check: NULL argument");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    if (p->S == 0 || p->Bt == 0)
+        return RNN_OK;
+    hipError_t e = hipStreamSynchronize((hipStream_t)hip_stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipStreamSynchronize");
+    int32_t err = 0;
+    const unsigned char *ws = (const unsigned char *)workspace;
+    e = hipMemcpy(&err, ws + p->ws.bar + (size_t)p->D * p->NBB * 4, 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return hip_fail(e, "error word read");
+    if (err) {
+        set_error("a step barrier timed out on the device");
+        return RNN_ERR_DEVICE;
+    }
+    return RNN_OK;
+}
+
+extern "C" rnn_status rnn_plan_enable_timing(rnn_plan *p, int32_t enable)
+{
+    if (!p) {
+        set_error("rnn_plan_enable_timing: NULL plan");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    p->timing = enable ? 1 : 0;
+    if (p->timing && p->dev_ready) {
+        for (int i = 0; i < 2 * STAGE_COUNT; ++i)
+            if (!p->events[i]) {
+                hipEvent_t ev;
+                hipError_t e = hipEventCreate(&ev);
+                if (e != hipSuccess)
+                    return hip_fail(e, "hipEventCreate");
+                p->events[i] = ev;
+            }
+    }
+    return RNN_OK;
+}
+
+extern "C" rnn_status rnn_plan_last_timings(rnn_plan *p, float *ms, int32_t n)
+{
+    if (!p || !ms) {
+        set_error("rnn_plan_last_timings: NULL argument");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    if (!p->events_recorded) {
+        set_error("rnn_plan_last_timings: no timed run");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    for (int i = 0; i < n && i < STAGE_COUNT; ++i) {
+        hipError_t e = hipEventSynchronize((hipEvent_t)p->events[2 * i + 1]);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipEventSynchronize");
+        float v = 0.0f;
+        e = hipEventElapsedTime(&v, (hipEvent_t)p->events[2 * i], (hipEvent_t)p->events[2 * i + 1]);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipEventElapsedTime");
+        ms[i] = v;
+    }
+    return RNN_OK;
+}
+
+extern "C" void rnn_plan_destroy(rnn_plan *p)
+{
+    if (!p)
+        return;
+    for (int i = 0; i < 2 * STAGE_COUNT; ++i)
+        if (p->events[i])
+            (void)hipEventDestroy((hipEvent_t)p->events[i]);
+    delete p;
+}

@@ -1,0 +1,328 @@
+"""Parity of the HIP path (through the C-ABI) with the CPU oracle.
+
+Floating point: |gpu - oracle| <= 2e-5 + 1e-4 * |oracle| element by element
+(fp32 projection), and for the bf16-projection workload both <= 2e-2 against
+the fp32 oracle and the fp32 bar against the oracle run with the same bf16
+rounding.  Masked positions (t >= sequence_lens[b]), zero-length rows and NaN
+bit patterns are compared bit for bit.  The two large workloads run at full
+size on the GPU in the benchmark's launch configuration and are checked on
+sampled batch rows, which the oracle computes on its own (rows are
+independent)."""
+import dataclasses
+import hashlib
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import recurrent_nn_amd as ra
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 2e-5, 1e-4
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ra._lib.load()
+    yield
+
+
+def u32(a):
+    return np.ascontiguousarray(a).view(np.uint32)
+
+
+def to_np(t):
+    return None if t is None else t.detach().cpu().numpy()
+
+
+def run_gpu(c, **extra):
+    say(f"  gpu run: {c.name} {extra}")
+    Y, Yh, Yc = ra.run_case(c, **extra)
+    torch.cuda.synchronize()
+    return to_np(Y), to_np(Yh), to_np(Yc)
+
+
+def check_close(got, ref, what, atol=ATOL, rtol=RTOL):
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    nan_r = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan_r), f"{what}: NaN positions differ"
+    if nan_r.any():
+        assert np.all(u32(got)[nan_r] == 0x7FC00000), f"{what}: NaN not canonical"
+    g, r = got[~nan_r].astype(np.float64), ref[~nan_r].astype(np.float64)
+    err = np.abs(g - r)
+    bad = err > atol + rtol * np.abs(r)
+    say(f"    {what}: max_abs={err.max() if err.size else 0:.3e} "
+        f"max_rel(|o|>=0.2)={(err / np.maximum(np.abs(r), 0.2)).max() if err.size else 0:.3e} "
+        f"bad={int(bad.sum())}/{err.size}")
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements outside {atol} + {rtol}|o|"
+
+
+def y_positions(c, Y, d, b):
+    """Y[t, d, b, :] over t for either layout."""
+    return Y[:, d, b] if c.layout == 0 else Y[b, :, d]
+
+
+def check_masks(c, Y, Yh, Yc):
+    """Bit-exact: +0.0 at t >= len_b, and zero final states for len_b = 0."""
+    if c.sequence_lens is None:
+        return
+    lens = c.sequence_lens.numpy()
+    D = int(c.W.shape[0])
+    for d in range(D):
+        for b, L in enumerate(lens):
+            tail = y_positions(c, Y, d, b)[L:]
+            assert np.all(u32(tail) == 0), f"Y not +0.0 past len at d={d} b={b}"
+            if L == 0:
+                sh = Yh[d, b] if c.layout == 0 else Yh[b, d]
+                assert np.all(u32(sh) == 0)
+                if Yc is not None:
+                    sc = Yc[d, b] if c.layout == 0 else Yc[b, d]
+                    assert np.all(u32(sc) == 0)
+
+
+def compare(c, gpu, ref=None, atol=ATOL, rtol=RTOL):
+    if ref is None:
+        _, *ref = oracle.run(c)
+    Y, Yh, Yc = gpu
+    check_close(Y, ref[0], "Y", atol, rtol)
+    check_close(Yh, ref[1], "Y_h", atol, rtol)
+    if c.op == "LSTM":
+        check_close(Yc, ref[2], "Y_c", atol, rtol)
+    check_masks(c, Y, Yh, Yc)
+
+
+# ---------------------------------------------------------------------------
+# The named workloads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["rnn_fwd_s4_b2_i3_h5", "lstm_bidir_s16_b4_i32_h64",
+                                  "gru_fwd_s128_b32_i256_h512_lbr0",
+                                  "gru_fwd_s128_b32_i256_h512_lbr1"])
+def test_small_workloads_match_oracle(name):
+    c = workloads.workload(name)
+    say(f"case {name}")
+    compare(c, run_gpu(c))
+
+
+def _sampled(name, rows, gpu_extra=None, bf16_ref=False):
+    full = workloads.workload(name)
+    say(f"case {name} full size on the GPU, oracle on rows {rows}")
+    Y, Yh, Yc = run_gpu(full, **(gpu_extra or {}))
+    sub = workloads.select_rows(full, rows)
+    _, Yo, Yho, Yco = oracle.run(sub)
+    pick = lambda A: A[:, :, rows] if full.layout == 0 else A[rows]
+    pick_s = lambda A: A[:, rows] if full.layout == 0 else A[rows]
+    got = (np.ascontiguousarray(pick(Y)), np.ascontiguousarray(pick_s(Yh)),
+           None if Yc is None else np.ascontiguousarray(pick_s(Yc)))
+    return full, sub, got, (Yo, Yho, Yco), (Y, Yh, Yc)
+
+
+def test_lstm_bench_workload_sampled_rows():
+    full, sub, got, ref, whole = _sampled("lstm_bidir_s512_b64_i1024_h1024", [0, 29, 63])
+    compare(sub, got, ref)
+    assert np.isfinite(whole[0]).all() and np.isfinite(whole[1]).all()
+
+
+def test_gru_bf16_workload_sampled_rows():
+    name = "gru_rev_s256_b256_i2048_h2048_bf16"
+    full = workloads.workload(name)
+    lens = full.sequence_lens.numpy()
+    rows = [int(np.argmin(lens)), 1, 128, int(np.argmax(lens)), 255]
+    full, sub, got, ref, whole = _sampled(name, rows)
+    # against the oracle with the same bf16 rounding: the fp32 bar
+    compare(sub, got, ref)
+    # against the fp32 oracle: the bf16-projection bar
+    sub32 = dataclasses.replace(sub, proj_bf16=False)
+    _, *ref32 = oracle.run(sub32)
+    check_close(got[0], ref32[0], "Y vs fp32 oracle", atol=2e-2, rtol=0.0)
+    check_close(got[1], ref32[1], "Y_h vs fp32 oracle", atol=2e-2, rtol=0.0)
+    check_masks(full, *whole)
+
+
+# ---------------------------------------------------------------------------
+# Features, ragged shapes and edge cases
+# ---------------------------------------------------------------------------
+
+FEATURES = [
+    dict(op="RNN", direction="forward", S=9, Bt=70, I=45, H=70, activations=["Relu"]),
+    dict(op="RNN", direction="bidirectional", S=6, Bt=5, I=8, H=33, layout=1, with_lens=True,
+         activations=["Affine", "LeakyRelu"], alpha=[0.8, 0.1], beta=[0.05]),
+    dict(op="GRU", direction="forward", S=8, Bt=20, I=12, H=200, with_lens=True,
+         linear_before_reset=0, clip=0.7),
+    dict(op="GRU", direction="reverse", S=7, Bt=37, I=24, H=96, with_lens=True,
+         linear_before_reset=1, layout=1),
+    dict(op="GRU", direction="bidirectional", S=5, Bt=66, I=16, H=40, linear_before_reset=0,
+         activations=["HardSigmoid", "Softsign", "Sigmoid", "Elu"], alpha=[0.3, 0.8], beta=[0.45]),
+    dict(op="LSTM", direction="forward", S=6, Bt=17, I=20, H=130, with_p=True, clip=0.8,
+         with_lens=True),
+    dict(op="LSTM", direction="bidirectional", S=5, Bt=9, I=7, H=64, with_p=True, input_forget=1,
+         layout=1, with_lens=True),
+    dict(op="LSTM", direction="reverse", S=4, Bt=3, I=5, H=11,
+         activations=["HardSigmoid", "LeakyRelu", "ScaledTanh"], alpha=[0.3, 0.2, 1.2],
+         beta=[0.4, 0.7], with_lens=True),
+    dict(op="LSTM", direction="forward", S=3, Bt=4, I=6, H=9,
+         activations=["ThresholdedRelu", "Softplus", "Relu"], alpha=[0.1]),
+    dict(op="RNN", direction="forward", S=5, Bt=3, I=4, H=6, with_bias=False,
+         activations=["Elu"], alpha=[0.5]),
+    dict(op="GRU", direction="forward", S=4, Bt=2, I=3, H=7, with_bias=False, with_h0=False,
+         linear_before_reset=1, activations=["Sigmoid", "ScaledTanh"], alpha=[1.3], beta=[0.6]),
+    dict(op="LSTM", direction="forward", S=24, Bt=32, I=64, H=512, with_lens=True),
+]
+
+
+@pytest.mark.parametrize("k", range(len(FEATURES)))
+def test_feature_cases_match_oracle(k):
+    spec = dict(FEATURES[k])
+    op, direction = spec.pop("op"), spec.pop("direction")
+    S, Bt, I, H = spec.pop("S"), spec.pop("Bt"), spec.pop("I"), spec.pop("H")
+    lay = spec.pop("layout", 0)
+    kw = {key: spec.pop(key) for key in ("with_lens", "with_p", "with_bias", "with_h0") if key in spec}
+    kw.setdefault("with_h0", True)
+    # weights ~ U(+-1.5/sqrt(H)) (at most 0.6) keep the recurrence contractive,
+    # as in the named workloads, so that fp32 rounding differences do not grow
+    c = workloads.random_case(op, direction, S, Bt, I, H, seed=500 + k, layout=lay,
+                              with_c0=(op == "LSTM"), scale=min(0.6, 1.5 / H ** 0.5),
+                              **kw, **spec)
+    say(f"case {c.name} {FEATURES[k]}")
+    compare(c, run_gpu(c))
+
+
+def test_zero_length_rows_and_masks_bit_exact():
+    c = workloads.random_case("LSTM", "bidirectional", 9, 19, 10, 24, seed=7, with_h0=True,
+                              with_c0=True, lens=[0, 9, 1, 0, 5, 2, 9, 0, 3, 4, 8, 7, 6, 1, 0, 9, 2,
+                                                  5, 3])
+    say(f"case {c.name}")
+    compare(c, run_gpu(c))
+
+
+def test_nan_is_canonical_on_gpu():
+    c = workloads.random_case("GRU", "bidirectional", 6, 5, 8, 20, seed=3, with_h0=True,
+                              lens=[6, 3, 0, 1, 5], linear_before_reset=1)
+    X = c.X.numpy().copy()
+    X.view(np.uint32)[2, 0, 1] = 0xFFC00123          # a negative NaN with payload
+    c.X = torch.from_numpy(X)
+    say(f"case {c.name} with an injected NaN")
+    compare(c, run_gpu(c))
+
+
+@pytest.mark.parametrize("op", ["RNN", "GRU", "LSTM"])
+def test_zero_size_on_gpu(op):
+    c = workloads.random_case(op, "bidirectional", 0, 3, 4, 5, seed=1, with_h0=True,
+                              with_c0=(op == "LSTM"))
+    say(f"case {c.name}")
+    Y, Yh, Yc = run_gpu(c)
+    assert Y.size == 0
+    assert np.array_equal(u32(Yh), u32(c.initial_h.numpy()))
+    if op == "LSTM":
+        assert np.array_equal(u32(Yc), u32(c.initial_c.numpy()))
+    c = workloads.random_case(op, "forward", 4, 0, 4, 5, seed=1)
+    Y, Yh, Yc = run_gpu(c)
+    assert Y.size == 0 and Yh.size == 0
+
+
+# ---------------------------------------------------------------------------
+# Paths, grid sizes, determinism and the invariants on the GPU path
+# ---------------------------------------------------------------------------
+
+def _digest(out):
+    h = hashlib.sha256()
+    for a in out:
+        if a is not None:
+            h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
+
+
+@pytest.mark.parametrize("op,attrs", [("LSTM", {}), ("GRU", dict(linear_before_reset=0)),
+                                      ("GRU", dict(linear_before_reset=1)), ("RNN", {})])
+def test_persistent_and_per_step_paths_agree_bitwise(op, attrs):
+    c = workloads.random_case(op, "bidirectional", 11, 40, 24, 96, seed=9, with_lens=True,
+                              with_h0=True, with_c0=(op == "LSTM"), with_p=(op == "LSTM"), **attrs)
+    say(f"case {c.name}")
+    a = run_gpu(c, kernel_path=ra.RNN_PATH_PERSISTENT)
+    b = run_gpu(c, kernel_path=ra.RNN_PATH_PER_STEP)
+    assert _digest(a) == _digest(b)
+    compare(c, a)
+
+
+def test_results_do_not_depend_on_the_grid():
+    c = workloads.random_case("LSTM", "bidirectional", 7, 50, 32, 128, seed=13, with_lens=True,
+                              with_h0=True, with_c0=True)
+    say(f"case {c.name}")
+    digests = set()
+    for upb, bt in [(0, 0), (1, 16), (3, 32), (4, 64), (8, 16)]:
+        digests.add(_digest(run_gpu(c, units_per_block=upb, batch_tile=bt)))
+    assert len(digests) == 1
+
+
+def test_repeated_runs_are_bit_identical():
+    c = workloads.workload("gru_fwd_s128_b32_i256_h512_lbr0")
+    say(f"case {c.name}")
+    plan = ra.plan_for_case(c)
+    outs = set()
+    for _ in range(3):
+        Y, Yh, _ = ra.run_case(c, plan=plan)
+        torch.cuda.synchronize()
+        outs.add(_digest((to_np(Y), to_np(Yh))))
+    assert len(outs) == 1
+    plan.check()
+
+
+def test_invariants_hold_bitwise_on_gpu():
+    c = workloads.random_case("GRU", "reverse", 8, 6, 10, 24, seed=21, with_h0=True,
+                              lens=[8, 5, 1, 0, 7, 3], linear_before_reset=0)
+    say(f"case {c.name}")
+    Y, Yh, _ = run_gpu(c)
+    # reverse == forward on per-row flipped input
+    f = dataclasses.replace(c, direction="forward")
+    X = c.X.clone()
+    for b, L in enumerate(c.sequence_lens.tolist()):
+        X[:L, b] = c.X[:L, b].flip(0)
+    f.X = X
+    Yf, Yhf, _ = run_gpu(f)
+    for b, L in enumerate(c.sequence_lens.tolist()):
+        assert np.array_equal(u32(Y[:L, 0, b]), u32(Yf[:L, 0, b][::-1]))
+    assert np.array_equal(u32(Yh), u32(Yhf))
+    # layout 1 == transposed layout 0
+    t = dataclasses.replace(c, layout=1)
+    t.X = c.X.transpose(0, 1).contiguous()
+    t.initial_h = c.initial_h.transpose(0, 1).contiguous()
+    Y1, Yh1, _ = run_gpu(t)
+    assert np.array_equal(u32(Y1), u32(np.ascontiguousarray(Y.transpose(2, 0, 1, 3))))
+    # state carry: (S1 + S2) == S1 then S2 from Y_h (forward, full length)
+    g = workloads.random_case("LSTM", "forward", 9, 6, 10, 24, seed=22, with_h0=True, with_c0=True)
+    Yg, Yhg, Ycg = run_gpu(g)
+    a = dataclasses.replace(g, seq=4)
+    a.X = g.X[:4].contiguous()
+    Ya, Yha, Yca = run_gpu(a)
+    b = dataclasses.replace(g, seq=5)
+    b.X = g.X[4:].contiguous()
+    b.initial_h, b.initial_c = torch.from_numpy(Yha), torch.from_numpy(Yca)
+    Yb, Yhb, Ycb = run_gpu(b)
+    assert np.array_equal(u32(Yg), u32(np.concatenate([Ya, Yb])))
+    assert np.array_equal(u32(Ycg), u32(Ycb))
+
+
+def test_constant_weights_are_packed_once_and_reused():
+    c = workloads.random_case("LSTM", "forward", 5, 8, 16, 32, seed=5, with_h0=True)
+    say(f"case {c.name}")
+    plan = ra.plan_for_case(c, constant_weights=True)
+    plan.enable_timing(True)
+    a = ra.run_case(c, plan=plan)
+    torch.cuda.synchronize()
+    b = ra.run_case(c, plan=plan)
+    torch.cuda.synchronize()
+    assert _digest([to_np(x) for x in a]) == _digest([to_np(x) for x in b])
+    t = plan.last_timings()
+    assert set(t) == set(ra.STAGES) and all(v >= 0 for v in t.values())
+    compare(c, [to_np(x) for x in b])
