@@ -27,8 +27,9 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-ffp-contract=off",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]
 
-HIP_SOURCES = ["recurrence_res.hip", "recurrence_s8.hip", "recurrence_s2.hip", "proj_gemm.hip",
-               "pack.hip", "recurrence.hip", "run.cpp"]
+# every .hip file of csrc (the step-loop instantiations are split over several
+# translation units so that they compile in parallel) and the HIP host code
+HIP_SOURCES = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip")) + ["run.cpp"]
 CXX_SOURCES = ["plan.cpp"]
 
 

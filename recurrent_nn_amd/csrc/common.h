@@ -38,12 +38,12 @@ struct Layout {
     size_t rp = 0;      // packed R: [D][NUB][NT*16][Hp] f32, zero-padded
     size_t xb = 0;      // X rounded to bf16 (bf16 projection only): [S*Bt][I]
     size_t xw = 0;      // projections: [D][S][Bt][G*H] f32, block-column order
-    size_t hbuf = 0;    // H exchange, ping-pong: [2][D][Btp][Hp] f32
-    size_t sbuf = 0;    // GRU lbr=0: r (.) H_prev exchange [D][Btp][Hp]
+    size_t hbuf = 0;    // H history: plane j = H before step j, [S+1][D][Btp][Hp] f32
+    size_t sbuf = 0;    // GRU lbr=0: r (.) H_prev of step j in plane j, [S][D][Btp][Hp]
     size_t cbuf = 0;    // LSTM cell state between launches [D][Bt][H]
     size_t zbuf = 0;    // GRU lbr=0 update gate between launches [D][Bt][H]
     size_t lens = 0;    // int32 [Bt]
-    size_t bar = 0;     // uint32 barrier counters [D*NBB], then int32 error word
+    size_t bar = 0;     // uint32 step flags [D*NBB*NUB], then int32 error word
     size_t total = 0;
 };
 
@@ -167,7 +167,7 @@ struct RecArgs {
 // persistent: one cooperative launch covering every phase; else one phase.
 int launch_recurrence(const RecArgs &a, int resident, int persistent, void *stream);
 int recurrence_can_persist(const RecArgs &a, int resident, int device, int *ok);
-bool recurrence_supported(int mt, int nt, int kb, int bt, int u, int resident);
+bool recurrence_supported(int mt, int nt, int nta, int phases, int kb, int bt, int u, int resident);
 
 struct FinalArgs {
     const float *h0, *c0;

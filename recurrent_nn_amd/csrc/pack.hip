@@ -137,18 +137,18 @@ int launch_cast_bf16(const float *X, uint16_t *Xb, int64_t n, void *stream)
     return (int)hipGetLastError();
 }
 
-// Exchange buffers and states before the first step: hbuf plane 0 holds
-// initial_h (zero when absent), everything else in hbuf / sbuf is zero (the
-// padding rows and columns must stay zero: they meet zero rows of R), cbuf
-// holds initial_c, and the barrier counters and the error word are cleared.
+// States before the first step: plane 0 of the H history holds initial_h
+// (zero when absent, and zero in the padding rows and columns), cbuf holds
+// initial_c, and the step flags and the error word are cleared.  Later planes
+// are written by the steps themselves.
 __global__ void init_kernel(InitArgs a)
 {
     const int64_t plane = a.D * a.Btp * a.Hp;
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = tid; i < 2 * plane; i += stride) {
+    for (int64_t i = tid; i < plane; i += stride) {
         float v = 0.0f;
-        if (i < plane && a.h0) {
+        if (a.h0) {
             const int64_t k = i % a.Hp;
             const int64_t b = (i / a.Hp) % a.Btp;
             const int64_t d = i / (a.Hp * a.Btp);
@@ -156,8 +156,6 @@ __global__ void init_kernel(InitArgs a)
                 v = a.layout == 0 ? a.h0[(d * a.Bt + b) * a.H + k] : a.h0[(b * a.D + d) * a.H + k];
         }
         a.hbuf[i] = v;
-        if (a.sbuf && i < plane)
-            a.sbuf[i] = 0.0f;
     }
     if (a.cbuf) {
         const int64_t n = a.D * a.Bt * a.H;
@@ -181,7 +179,7 @@ __global__ void init_kernel(InitArgs a)
 
 int launch_init(const InitArgs &a, void *stream)
 {
-    const int64_t work = 2 * a.D * a.Btp * a.Hp;
+    const int64_t work = a.D * a.Btp * a.Hp;
     int64_t blocks = (work + 255) / 256;
     if (blocks > 4096)
         blocks = 4096;

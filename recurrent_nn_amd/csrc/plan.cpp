@@ -136,15 +136,20 @@ void tiles_for(const rnn_plan &p, int uc, int *nta, int *ntb)
 // The recurrence kernel is compiled for these shapes only (recurrence.hip).
 // R in registers: 2 or 4 row tiles, 1 or 2 column tiles, 8 or 16 k blocks of
 // 16 per wave, at most 2 (row, unit) pairs per thread.
-bool resident_ok(int nt, int kb, int mt, int pairs)
+bool resident_ok(int nt, int nta, int phases, int kb, int mt, int pairs)
 {
-    return (mt == 2 || mt == 4) && nt <= 2 && (kb == 8 || kb == 16) && pairs <= 2;
+    const bool tiles = phases == 1 ? nt <= 2 : (nt == 2 && nta == 1 && mt == 2);
+    return (mt == 2 || mt == 4) && tiles && (kb == 8 || kb == 16) && pairs <= 2;
 }
 
-// R streamed every step: 1, 2, 4 or 6 column tiles, at most 8 pairs.
-bool streamed_ok(int nt, int pairs)
+// R streamed every step: 1, 2, 4 or 6 column tiles for one phase; for two
+// (GRU lbr=0) 1+1, 2+1 or 4+2; at most 8 pairs.
+bool streamed_ok(int nt, int nta, int phases, int pairs)
 {
-    return (nt == 1 || nt == 2 || nt == 4 || nt == 6) && pairs <= kMaxPairs;
+    const bool tiles = phases == 1 ? (nt == 1 || nt == 2 || nt == 4 || nt == 6)
+                                   : ((nt == 2 && nta == 1) || (nt == 3 && nta == 2) ||
+                                      (nt == 6 && nta == 4));
+    return tiles && pairs <= kMaxPairs;
 }
 
 // Choose units per workgroup: at most kMaxWorkgroups workgroups, the least
@@ -178,10 +183,10 @@ rnn_status choose_tiling(const rnn_attrs &a, rnn_plan &p)
         tiles_for(p, u, nta, ntb);
         int nt = *nta + *ntb;
         int pairs = (p.BT * u + kThreads - 1) / kThreads;
-        *res = resident_ok(nt, p.KB, p.MT, pairs);
-        if (!*res && !streamed_ok(nt, pairs))
+        *res = resident_ok(nt, *nta, p.phases, p.KB, p.MT, pairs);
+        if (!*res && !streamed_ok(nt, *nta, p.phases, pairs))
             return false;
-        long lds = ((long)kWaves * p.BT * (nt * 16 + 4) + 3L * p.BT * u + p.BT) * 4;
+        long lds = ((long)kWaves * p.BT * (nt * 16 + 4) + 3L * p.BT * u + p.BT + 11L * u) * 4;
         if (lds > 160 * 1024)
             return false;
         *cost = (long)p.MT * nt * p.KB * 16 + (*res ? 0 : (long)p.MT * nt * p.KB * 4);
@@ -253,12 +258,12 @@ void make_layout(rnn_plan &p)
     L.rp = take((size_t)p.D * p.NUB * p.NT * 16 * p.Hp * 4);
     L.xb = take(0);   // X is rounded to bf16 inside the projection's staging
     L.xw = take((size_t)p.D * p.S * p.Bt * GH * 4);
-    L.hbuf = take((size_t)2 * p.D * p.Btp * p.Hp * 4);
-    L.sbuf = take(p.phases == 2 ? (size_t)p.D * p.Btp * p.Hp * 4 : 0);
+    L.hbuf = take((size_t)(p.S + 1) * p.D * p.Btp * p.Hp * 4);
+    L.sbuf = take(p.phases == 2 ? (size_t)p.S * p.D * p.Btp * p.Hp * 4 : 0);
     L.cbuf = take(p.op == RNN_OP_LSTM ? (size_t)p.D * p.Bt * p.H * 4 : 0);
     L.zbuf = take(p.phases == 2 ? (size_t)p.D * p.Bt * p.H * 4 : 0);
     L.lens = take((size_t)std::max<int64_t>(p.Bt, 1) * 4);
-    L.bar = take((size_t)(p.D * p.NBB + 1) * 4);
+    L.bar = take((size_t)(p.D * p.NBB * p.NUB + 1) * 4);
     L.total = off;
 }
 

@@ -7,27 +7,79 @@
 
 namespace rnnamd {
 
-rec_fn rec_get_resident(int mt, int nt, int kb);
-rec_fn rec_get_streamed2(int mt, int nt);
-rec_fn rec_get_streamed8(int mt, int nt);
+#define RNN_DECL(A)                                                                               \
+    rec_fn rec_get_resident_a##A(int mt, int nt, int kb, int ta);                                 \
+    rec_fn rec_get_streamed2_a##A(int mt, int nt, int ta);                                        \
+    rec_fn rec_get_streamed8_a##A(int mt, int nt, int ta);
+RNN_DECL(0)
+RNN_DECL(1)
+RNN_DECL(2)
+RNN_DECL(3)
+#undef RNN_DECL
+
+// Activation set compiled into the kernel: 1 Sigmoid/Tanh(/Tanh) for LSTM
+// and GRU, 2 HardSigmoid/Tanh for GRU, 3 Tanh for RNN, 0 anything else.
+static int act_set(const RecArgs &a)
+{
+    bool same = true;                      // both directions use the same kinds
+    for (int d = 1; d < a.D; ++d)
+        for (int k = 0; k < 3; ++k)
+            same = same && a.act[d][k].kind == a.act[0][k].kind;
+    if (!same)
+        return 0;
+    const int f = a.act[0][0].kind, g = a.act[0][1].kind, h = a.act[0][2].kind;
+    if (a.op == RNN_OP_LSTM && f == ACT_SIGMOID && g == ACT_TANH && h == ACT_TANH)
+        return 1;
+    if (a.op == RNN_OP_GRU && f == ACT_SIGMOID && g == ACT_TANH)
+        return 1;
+    if (a.op == RNN_OP_GRU && f == ACT_HARDSIGMOID && g == ACT_TANH)
+        return 2;
+    if (a.op == RNN_OP_RNN && f == ACT_TANH)
+        return 3;
+    return 0;
+}
+
+static rec_fn get_resident(int act, int mt, int nt, int kb, int ta)
+{
+    switch (act) {
+    case 1: return rec_get_resident_a1(mt, nt, kb, ta);
+    case 2: return rec_get_resident_a2(mt, nt, kb, ta);
+    case 3: return rec_get_resident_a3(mt, nt, kb, ta);
+    default: return rec_get_resident_a0(mt, nt, kb, ta);
+    }
+}
+
+static rec_fn get_streamed(int act, int p, int mt, int nt, int ta)
+{
+    switch (act) {
+    case 1: return p == 2 ? rec_get_streamed2_a1(mt, nt, ta) : rec_get_streamed8_a1(mt, nt, ta);
+    case 2: return p == 2 ? rec_get_streamed2_a2(mt, nt, ta) : rec_get_streamed8_a2(mt, nt, ta);
+    case 3: return p == 2 ? rec_get_streamed2_a3(mt, nt, ta) : rec_get_streamed8_a3(mt, nt, ta);
+    default: return p == 2 ? rec_get_streamed2_a0(mt, nt, ta) : rec_get_streamed8_a0(mt, nt, ta);
+    }
+}
 
 static rec_fn pick(const RecArgs &a, int resident)
 {
     const int np = (a.BT * a.U + kThreads - 1) / kThreads;
+    const int ta = a.phases == 2 ? a.NTA : 0;
+    const int act = act_set(a);
     if (resident)
-        return np <= 2 ? rec_get_resident(a.MT, a.NT, a.KB) : nullptr;
+        return np <= 2 ? get_resident(act, a.MT, a.NT, a.KB, ta) : nullptr;
     if (np <= 2)
-        return rec_get_streamed2(a.MT, a.NT);
+        return get_streamed(act, 2, a.MT, a.NT, ta);
     if (np <= kMaxPairs)
-        return rec_get_streamed8(a.MT, a.NT);
+        return get_streamed(act, 8, a.MT, a.NT, ta);
     return nullptr;
 }
 
-bool recurrence_supported(int mt, int nt, int kb, int bt, int u, int resident)
+bool recurrence_supported(int mt, int nt, int nta, int phases, int kb, int bt, int u, int resident)
 {
     RecArgs a{};
     a.MT = mt;
     a.NT = nt;
+    a.NTA = nta;
+    a.phases = phases;
     a.KB = kb;
     a.BT = bt;
     a.U = u;
@@ -85,3 +137,4 @@ int launch_recurrence(const RecArgs &a, int resident, int persistent, void *stre
 }
 
 }  // namespace rnnamd
+

@@ -16,14 +16,20 @@
 // slice of R stays in registers for the whole sequence; otherwise it is
 // re-read (from L2 / the memory-side cache) every step.
 //
-// Steps.  The persistent form runs every step in one cooperative launch and
-// separates steps with a barrier among the workgroups of one (d, bb) group:
-// a monotonic counter with an agent-scope release before the arrival and an
-// acquire after the wait.  H is exchanged through a ping-pong buffer in
-// device memory.  GRU with linear_before_reset = 0 has two phases per step:
-// z and r first (their product over H), then the candidate's product over
-// r (.) H_prev, with a barrier in between.  The per-step form runs one phase
-// per launch, the kernel boundary being the barrier.
+// Steps.  The persistent form runs every step in one cooperative launch.  H
+// is exchanged through a history buffer in device memory: step j reads plane
+// j and writes plane j + 1 with agent-coherent (write-through) stores, so no
+// cache ever holds a stale copy of a plane and no whole-cache writeback or
+// invalidate is needed between steps.  Steps are separated by a barrier
+// among the workgroups of one (d, bb) group built on one flag per workgroup
+// (no contended counter).  GRU with linear_before_reset = 0 has two phases
+// per step: z and r first (their product over H), then the candidate's
+// product over r (.) H_prev, with a barrier in between.  The per-step form
+// runs one phase per launch, the kernel boundary being the barrier.
+//
+// Activation sets known per launch (the defaults, HardSigmoid/Tanh) are
+// compiled into their own kernels; any other set goes through a run-time
+// switch.
 //
 // Epilogue.  This file is compiled with -ffp-contract=off: every written
 // addition and multiplication is its own IEEE operation, in the written order
@@ -41,40 +47,142 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Barrier among the NUB workgroups of one (direction, batch block) group.
-// Returns false (and raises the error word) if the wait exceeded spin_limit.
-__device__ __forceinline__ void group_barrier(uint32_t *ctr, uint32_t target, int32_t *err,
-                                              uint32_t spin_limit, bool &dead)
+// Agent-coherent store (write-through to the device coherence point, no
+// dirty line left in this XCD's L2): how H and r (.) H_prev are published.
+__device__ __forceinline__ void store_coherent(float *p, float v)
 {
-    wait_stores();                 // this wave's stores have reached L2
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Step barrier among the NUB workgroups of one (direction, batch block)
+// group: each workgroup publishes "phase q done" in its own flag after its
+// coherent stores have completed, then one wave polls the group's flags.
+// No whole-cache writeback or invalidate is needed: every step writes a
+// fresh plane of the H history that no cache has seen before.  A wait longer
+// than spin_limit polls raises the error word and stops waiting.
+__device__ __forceinline__ void group_barrier(uint32_t *flags, int nub, int me, uint32_t target,
+                                              int32_t *err, uint32_t spin_limit, bool &dead)
+{
+    wait_stores();                 // this wave's coherent stores have completed
     __syncthreads();
-    if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");        // write L2 back
-        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (!dead) {
-            uint32_t n = 0;
-            while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-                __builtin_amdgcn_s_sleep(1);
-                if (++n > spin_limit) {
+    if (threadIdx.x == 0)
+        __hip_atomic_store(flags + me, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x < 64 && !dead) {
+        uint32_t n = 0;
+        for (;;) {
+            bool ok = true;
+            for (int i = threadIdx.x; i < nub; i += 64)
+                ok = ok && __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target;
+            if (__all(ok))
+                break;
+            __builtin_amdgcn_s_sleep(1);
+            if (++n > spin_limit) {
+                if (threadIdx.x == 0)
                     __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    dead = true;
-                    break;
-                }
+                dead = true;
+                break;
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");        // drop stale lines
     }
     __syncthreads();
+}
+
+// The step product over one wave's k range, R in registers: acc[mt][nt] for
+// the compile-time tile range [T0, T1), with A tiles prefetched PD k blocks
+// ahead; `mid` runs right after the last A prefetch is issued (used to issue
+// the loads the epilogue needs, after every load the product waits on).
+template <int MT, int NT, int KBR, int T0, int T1, int PD, typename Mid>
+__device__ __forceinline__ void product_res(f4 (&acc)[MT][NT], const float *asrc, int Hp,
+                                            const f4 (&rr)[NT][KBR], Mid mid)
+{
+    // 16-k blocks; lane (r, q) supplies k = 16*kb + 4q + s of row r
+    constexpr int D_ = PD < KBR ? PD : KBR;
+    f4 ring[D_ + 1][MT];
+#pragma unroll
+    for (int p = 0; p < D_; ++p)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            ring[p][mt] = *(const f4 *)(asrc + (size_t)mt * 16 * Hp + p * 16);
+    if constexpr (D_ >= KBR)
+        mid();
+#pragma unroll
+    for (int kb = 0; kb < KBR; ++kb) {
+        if (kb + D_ < KBR) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                ring[(kb + D_) % (D_ + 1)][mt] =
+                    *(const f4 *)(asrc + (size_t)mt * 16 * Hp + (kb + D_) * 16);
+            if (kb + D_ == KBR - 1)
+                mid();
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int nt = T0; nt < T1; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                        ring[kb % (D_ + 1)][mt][s], rr[nt][kb][s], acc[mt][nt], 0, 0, 0);
+    }
+}
+
+// The same with R streamed from memory every step (runtime KB).
+template <int MT, int NT, int T0, int T1, typename Mid>
+__device__ __forceinline__ void product_stream(f4 (&acc)[MT][NT], const float *asrc,
+                                               const float *rfrag, int Hp, int KB, Mid mid)
+{
+    f4 av[MT], bv[NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        av[mt] = *(const f4 *)(asrc + (size_t)mt * 16 * Hp);
+#pragma unroll
+    for (int nt = T0; nt < T1; ++nt)
+        bv[nt] = *(const f4 *)(rfrag + (size_t)nt * 16 * Hp);
+    if (KB == 1)
+        mid();
+    for (int kb = 0; kb < KB; ++kb) {
+        f4 an[MT], bn[NT];
+        if (kb + 1 < KB) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                an[mt] = *(const f4 *)(asrc + (size_t)mt * 16 * Hp + (kb + 1) * 16);
+#pragma unroll
+            for (int nt = T0; nt < T1; ++nt)
+                bn[nt] = *(const f4 *)(rfrag + (size_t)nt * 16 * Hp + (kb + 1) * 16);
+            if (kb + 2 == KB)
+                mid();
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int nt = T0; nt < T1; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt][s], bv[nt][s],
+                                                                       acc[mt][nt], 0, 0, 0);
+        if (kb + 1 < KB) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                av[mt] = an[mt];
+#pragma unroll
+            for (int nt = T0; nt < T1; ++nt)
+                bv[nt] = bn[nt];
+        }
+    }
 }
 
 // LDS bytes of one workgroup: the four partial tiles, then the per-pair
 // states (h, c, z) and the per-row lengths.
 __host__ __device__ inline size_t rec_lds_bytes(int bt, int nt, int u)
 {
-    return ((size_t)kWaves * bt * (nt * 16 + 4) + 3 * (size_t)bt * u + bt) * 4;
+    return ((size_t)kWaves * bt * (nt * 16 + 4) + 3 * (size_t)bt * u + bt + 11 * (size_t)u) * 4;
 }
 
-template <int MT, int NT, int KBR, int P>
+// Depth (in 16-k blocks) of the A-operand prefetch of the register-resident
+// product; deeper rings measured no faster and cost registers.
+constexpr int kPrefetch = 1;
+
+template <int MT, int NT, int KBR, int P, int TA, int ACT>
 __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
 {
     constexpr bool RES = KBR > 0;
@@ -88,6 +196,7 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
     float *cst = hst + BT * a.U;                 // [BT * U] LSTM cell state
     float *zst = cst + BT * a.U;                 // [BT * U] GRU update gate between phases
     int *lst = (int *)(zst + BT * a.U);          // [BT] sequence length of each row
+    float *cst_u = (float *)(lst + BT);          // [11][U] Wb, Rb per gate, then Pi, Po, Pf
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -110,10 +219,11 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
     const bool rev = a.reverse_only || d == 1;
     const int GH = a.G * a.H;
     const int op = a.op;
-    const size_t plane = (size_t)a.D * a.Btp * Hp;           // one hbuf plane
+    const size_t plane = (size_t)a.D * a.Btp * Hp;           // one plane of the H history
     const size_t drow = ((size_t)d * a.Btp + row0) * Hp;     // this group's rows
     const int grp = d * a.NBB + bb;
     const ActSpec fa = a.act[d][0], ga = a.act[d][1], ha = a.act[d][2];
+
     const float *Wb = a.B ? a.B + (size_t)d * 2 * GH : nullptr;
     const float *Rb = a.B ? Wb + GH : nullptr;
     const float *Pd = a.P ? a.P + (size_t)d * 3 * a.H : nullptr;
@@ -138,7 +248,7 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
         for (int pi = tid; pi < npairs; pi += kThreads) {
             const int rl = pi / uc, u = pi - rl * uc;
             const int b = row0 + rl;
-            hst[pi] = a.hbuf[(size_t)(j0 & 1) * plane + drow + (size_t)rl * Hp + u0 + u];
+            hst[pi] = a.hbuf[(size_t)j0 * plane + drow + (size_t)rl * Hp + u0 + u];
             cst[pi] = op == RNN_OP_LSTM ? a.cbuf[((size_t)d * a.Bt + b) * a.H + u0 + u] : 0.0f;
             zst[pi] = (a.phases == 2 && (a.q_begin % 2) == 1)
                           ? a.zbuf[((size_t)d * a.Bt + b) * a.H + u0 + u]
@@ -146,11 +256,21 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
         }
         for (int rl = tid; rl < rows; rl += kThreads)
             lst[rl] = a.lens[row0 + rl];
+        for (int e = tid; e < 11 * uc; e += kThreads) {
+            const int k = e / uc, u = e - k * uc;
+            float v = 0.0f;
+            if (k < 4 && k < a.G && Wb)
+                v = Wb[k * a.H + u0 + u];
+            else if (k >= 4 && k < 8 && k - 4 < a.G && Rb)
+                v = Rb[(k - 4) * a.H + u0 + u];
+            else if (k >= 8 && Pd)
+                v = Pd[(k - 8) * a.H + u0 + u];
+            cst_u[k * a.U + u] = v;
+        }
         __syncthreads();
     }
 
     bool dead = false;
-    const uint32_t nub = (uint32_t)a.NUB;
     for (int q = a.q_begin; q < a.q_end; ++q) {
         const int j = q / a.phases;
         const int ph = q - j * a.phases;
@@ -177,17 +297,19 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
             }
         };
         float xw[kPrefetchXW ? P : 1][4];
-        if constexpr (kPrefetchXW) {
+        auto prefetch_xw = [&]() {
+            if constexpr (kPrefetchXW) {
 #pragma unroll
-            for (int i = 0; i < P; ++i) {
-                const int pi = tid + kThreads * i;
-                if (pi < npairs)
-                    fetch_xw(pi, xw[i]);
+                for (int i = 0; i < P; ++i) {
+                    const int pi = tid + kThreads * i;
+                    if (pi < npairs)
+                        fetch_xw(pi, xw[i]);
+                }
             }
-        }
+        };
 
         // ---- the product over this wave's k range --------------------------
-        const float *asrc = (ph == 0 ? a.hbuf + (size_t)(j & 1) * plane : a.sbuf) + drow +
+        const float *asrc = (ph == 0 ? a.hbuf : a.sbuf) + (size_t)j * plane + drow +
                             (size_t)lr * Hp + w * KB * 16 + 4 * lq;
         f4 acc[MT][NT];
 #pragma unroll
@@ -195,84 +317,26 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
                 acc[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
-
-        f4 av[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            av[mt] = *(const f4 *)(asrc + (size_t)mt * 16 * Hp);
+        // phase tiles: [0, NT) for one phase, [0, TA) then [TA, NT) for two
+        constexpr int TA0 = TA > 0 ? TA : NT;
         if constexpr (RES) {
-#pragma unroll
-            for (int kb = 0; kb < KBR; ++kb) {
-                f4 an[MT];
-                if (kb + 1 < KBR) {
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        an[mt] = *(const f4 *)(asrc + (size_t)mt * 16 * Hp + (kb + 1) * 16);
-                }
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        if (nt < t0 || nt >= t1)
-                            continue;
-#pragma unroll
-                        for (int mt = 0; mt < MT; ++mt)
-                            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                av[mt][s], rr[nt][kb][s], acc[mt][nt], 0, 0, 0);
-                    }
-                if (kb + 1 < KBR) {
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        av[mt] = an[mt];
-                }
-            }
+            if (ph == 0)
+                product_res<MT, NT, KBR, 0, TA0, kPrefetch>(acc, asrc, Hp, rr, prefetch_xw);
+            else if constexpr (TA > 0)
+                product_res<MT, NT, KBR, TA, NT, kPrefetch>(acc, asrc, Hp, rr, prefetch_xw);
         } else {
-            f4 bv[NT];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                bv[nt] = (nt >= t0 && nt < t1) ? *(const f4 *)(rfrag + (size_t)nt * 16 * Hp)
-                                               : f4{0.f, 0.f, 0.f, 0.f};
-            for (int kb = 0; kb < KB; ++kb) {
-                f4 an[MT], bn[NT];
-                if (kb + 1 < KB) {
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        an[mt] = *(const f4 *)(asrc + (size_t)mt * 16 * Hp + (kb + 1) * 16);
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        bn[nt] = (nt >= t0 && nt < t1)
-                                     ? *(const f4 *)(rfrag + (size_t)nt * 16 * Hp + (kb + 1) * 16)
-                                     : f4{0.f, 0.f, 0.f, 0.f};
-                }
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        if (nt < t0 || nt >= t1)
-                            continue;
-#pragma unroll
-                        for (int mt = 0; mt < MT; ++mt)
-                            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                av[mt][s], bv[nt][s], acc[mt][nt], 0, 0, 0);
-                    }
-                if (kb + 1 < KB) {
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        av[mt] = an[mt];
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        bv[nt] = bn[nt];
-                }
-            }
+            if (ph == 0)
+                product_stream<MT, NT, 0, TA0>(acc, asrc, rfrag, Hp, KB, prefetch_xw);
+            else if constexpr (TA > 0)
+                product_stream<MT, NT, TA, NT>(acc, asrc, rfrag, Hp, KB, prefetch_xw);
         }
-
         // ---- partial tiles -> LDS, summed in wave order ----------------------
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 if (nt < t0 || nt >= t1)
-                    continue;
+                    continue;          // (uniform: the other phase's tiles)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     red[(w * BT + mt * 16 + 4 * lq + r) * LDR + nt * 16 + lr] = acc[mt][nt][r];
@@ -291,8 +355,9 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
         };
 
         // ---- gate arithmetic of one (row, unit) pair, in the written order --
-        float *hnext = a.hbuf + (size_t)((j + 1) & 1) * plane + drow;
-        auto do_pair = [&](int pi, const float *xv) {
+        float *hnext = a.hbuf + (size_t)(j + 1) * plane + drow;
+        float *snext = a.sbuf ? a.sbuf + (size_t)j * plane + drow : nullptr;
+        auto do_pair = [&](int pi, const float *xv, auto F, auto Gf, auto Hf) {
             const int rl = pi / uc, u = pi - rl * uc;
             const int b = row0 + rl;
             const int gu = u0 + u;                         // hidden unit
@@ -304,34 +369,34 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
                 if (op == RNN_OP_RNN) {
                     float pre = xv[0] + rec_at(rl, u);
                     if (Wb) {
-                        pre = pre + Wb[gu];
-                        pre = pre + Rb[gu];
+                        pre = pre + cst_u[u];
+                        pre = pre + cst_u[4 * a.U + u];
                     }
                     pre = clip_pre(pre, a.clip_on, a.clip);
-                    hn = act_apply(fa.kind, fa.alpha, fa.beta, pre);
+                    hn = F(pre);
                 } else if (op == RNN_OP_GRU) {
                     if (a.phases == 1) {                    // linear_before_reset = 1
                         float pz = xv[0] + rec_at(rl, u);
                         float pr = xv[1] + rec_at(rl, uc + u);
                         if (Wb) {
-                            pz = pz + Wb[gu];
-                            pz = pz + Rb[gu];
-                            pr = pr + Wb[a.H + gu];
-                            pr = pr + Rb[a.H + gu];
+                            pz = pz + cst_u[u];
+                            pz = pz + cst_u[4 * a.U + u];
+                            pr = pr + cst_u[a.U + u];
+                            pr = pr + cst_u[5 * a.U + u];
                         }
                         pz = clip_pre(pz, a.clip_on, a.clip);
                         pr = clip_pre(pr, a.clip_on, a.clip);
-                        const float z = act_apply(fa.kind, fa.alpha, fa.beta, pz);
-                        const float r = act_apply(fa.kind, fa.alpha, fa.beta, pr);
+                        const float z = F(pz);
+                        const float r = F(pr);
                         float rh = rec_at(rl, 2 * uc + u);
                         if (Wb)
-                            rh = rh + Rb[2 * a.H + gu];
+                            rh = rh + cst_u[6 * a.U + u];
                         const float gated = r * rh;
                         float ph_ = xv[2] + gated;
                         if (Wb)
-                            ph_ = ph_ + Wb[2 * a.H + gu];
+                            ph_ = ph_ + cst_u[2 * a.U + u];
                         ph_ = clip_pre(ph_, a.clip_on, a.clip);
-                        const float ht = act_apply(ga.kind, ga.alpha, ga.beta, ph_);
+                        const float ht = Gf(ph_);
                         const float omz = 1.0f - z;
                         const float a1 = omz * ht;
                         const float a2 = z * hp;
@@ -340,24 +405,24 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
                         float pz = xv[0] + rec_at(rl, u);
                         float pr = xv[1] + rec_at(rl, uc + u);
                         if (Wb) {
-                            pz = pz + Wb[gu];
-                            pz = pz + Rb[gu];
-                            pr = pr + Wb[a.H + gu];
-                            pr = pr + Rb[a.H + gu];
+                            pz = pz + cst_u[u];
+                            pz = pz + cst_u[4 * a.U + u];
+                            pr = pr + cst_u[a.U + u];
+                            pr = pr + cst_u[5 * a.U + u];
                         }
                         pz = clip_pre(pz, a.clip_on, a.clip);
                         pr = clip_pre(pr, a.clip_on, a.clip);
-                        zst[pi] = act_apply(fa.kind, fa.alpha, fa.beta, pz);
-                        const float r = act_apply(fa.kind, fa.alpha, fa.beta, pr);
-                        a.sbuf[drow + (size_t)rl * Hp + gu] = r * hp;   // r (.) H_prev
+                        zst[pi] = F(pz);
+                        const float r = F(pr);
+                        store_coherent(snext + (size_t)rl * Hp + gu, r * hp);   // r (.) H_prev
                     } else {                                // lbr = 0: candidate
                         float ph_ = xv[2] + rec_at(rl, a.NTA * 16 + u);
                         if (Wb) {
-                            ph_ = ph_ + Wb[2 * a.H + gu];
-                            ph_ = ph_ + Rb[2 * a.H + gu];
+                            ph_ = ph_ + cst_u[2 * a.U + u];
+                            ph_ = ph_ + cst_u[6 * a.U + u];
                         }
                         ph_ = clip_pre(ph_, a.clip_on, a.clip);
-                        const float ht = act_apply(ga.kind, ga.alpha, ga.beta, ph_);
+                        const float ht = Gf(ph_);
                         const float z = zst[pi];
                         const float omz = 1.0f - z;
                         const float a1 = omz * ht;
@@ -370,43 +435,43 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
                     for (int g = 0; g < 4; ++g) {
                         float v = xv[g] + rec_at(rl, g * uc + u);
                         if (Wb) {
-                            v = v + Wb[g * a.H + gu];
-                            v = v + Rb[g * a.H + gu];
+                            v = v + cst_u[g * a.U + u];
+                            v = v + cst_u[(4 + g) * a.U + u];
                         }
                         pre[g] = v;
                     }
                     const float cp = cn;
                     if (Pd) {
-                        const float pi_ = Pd[gu] * cp;
-                        const float pf_ = Pd[2 * a.H + gu] * cp;
+                        const float pi_ = cst_u[8 * a.U + u] * cp;
+                        const float pf_ = cst_u[10 * a.U + u] * cp;
                         pre[0] = pre[0] + pi_;
                         pre[2] = pre[2] + pf_;
                     }
                     const float ci = clip_pre(pre[0], a.clip_on, a.clip);
                     const float cf = clip_pre(pre[2], a.clip_on, a.clip);
                     const float cc = clip_pre(pre[3], a.clip_on, a.clip);
-                    const float ig = act_apply(fa.kind, fa.alpha, fa.beta, ci);
+                    const float ig = F(ci);
                     const float fg =
-                        a.input_forget ? 1.0f - ig : act_apply(fa.kind, fa.alpha, fa.beta, cf);
-                    const float ct = act_apply(ga.kind, ga.alpha, ga.beta, cc);
+                        a.input_forget ? 1.0f - ig : F(cf);
+                    const float ct = Gf(cc);
                     const float k1 = fg * cp;
                     const float k2 = ig * ct;
                     cn = k1 + k2;
                     float po = pre[1];
                     if (Pd) {
-                        const float pov = Pd[a.H + gu] * cn;
+                        const float pov = cst_u[9 * a.U + u] * cn;
                         po = po + pov;
                     }
                     po = clip_pre(po, a.clip_on, a.clip);
-                    const float og = act_apply(fa.kind, fa.alpha, fa.beta, po);
-                    const float hc = act_apply(ha.kind, ha.alpha, ha.beta, cn);
+                    const float og = F(po);
+                    const float hc = Hf(cn);
                     hn = og * hc;
                 }
             } else if (a.phases == 2 && ph == 0) {
-                a.sbuf[drow + (size_t)rl * Hp + gu] = 0.0f;
+                store_coherent(snext + (size_t)rl * Hp + gu, 0.0f);
             }
             if (last_phase) {
-                hnext[(size_t)rl * Hp + gu] = hn;           // carried unchanged when inactive
+                store_coherent(hnext + (size_t)rl * Hp + gu, hn);   // carried when inactive
                 hst[pi] = hn;
                 cst[pi] = cn;
                 if (a.Y) {
@@ -419,24 +484,44 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
             }
         };
 
-        if constexpr (kPrefetchXW) {
+        auto run_pairs = [&](auto F, auto Gf, auto Hf) {
+            if constexpr (kPrefetchXW) {
 #pragma unroll
-            for (int i = 0; i < P; ++i) {
-                const int pi = tid + kThreads * i;
-                if (pi < npairs)
-                    do_pair(pi, xw[i]);
-            }
-        } else {
+                for (int i = 0; i < P; ++i) {
+                    const int pi = tid + kThreads * i;
+                    if (pi < npairs)
+                        do_pair(pi, xw[i], F, Gf, Hf);
+                }
+            } else {
 #pragma unroll 1
-            for (int pi = tid; pi < npairs; pi += kThreads) {
-                float xv[4];
-                fetch_xw(pi, xv);
-                do_pair(pi, xv);
+                for (int pi = tid; pi < npairs; pi += kThreads) {
+                    float xv[4];
+                    fetch_xw(pi, xv);
+                    do_pair(pi, xv, F, Gf, Hf);
+                }
             }
+        };
+        // ACT (compile time): 1 Sigmoid/Tanh/Tanh, 2 HardSigmoid/Tanh, 3 Tanh,
+        // 0 any set through the run-time switch
+        if constexpr (ACT == 1)
+            run_pairs(ActSigmoid{}, ActTanh{}, ActTanh{});
+        else if constexpr (ACT == 2)
+            run_pairs(ActHardSigmoid{fa.alpha, fa.beta}, ActTanh{}, ActTanh{});
+        else if constexpr (ACT == 3)
+            run_pairs(ActTanh{}, ActTanh{}, ActTanh{});
+        else
+            run_pairs(ActAny{fa}, ActAny{ga}, ActAny{ha});
+        // The last unit block also writes the padding columns [H, Hp) of the
+        // plane it published, as zeros (they meet zero rows of R).
+        if (u0 + uc == a.H && Hp > a.H && (last_phase || a.phases == 2)) {
+            float *pl = last_phase ? hnext : snext;
+            const int padw = Hp - a.H;
+            for (int e = tid; e < rows * padw; e += kThreads)
+                store_coherent(pl + (size_t)(e / padw) * Hp + a.H + e % padw, 0.0f);
         }
-
         if (q + 1 < a.q_end)
-            group_barrier(a.bar + grp, nub * (uint32_t)(q + 1), a.err, a.spin_limit, dead);
+            group_barrier(a.bar + (size_t)grp * a.NUB, a.NUB, ub, (uint32_t)(q + 1), a.err,
+                          a.spin_limit, dead);
         else
             __syncthreads();
     }
