@@ -26,7 +26,7 @@
  *     library's own polynomials are not available).  Elu uses expm1 and
  *     Softplus log1p, the accurate binary64 evaluations of exp(x)-1 and
  *     log(1+exp(x)).
- *   - clip <= 0 (or NaN) clamps nothing ("when present and positive").
+ *   - clip <= 0 (or NaN) clamps nothing: clip acts only when given and positive.
  *   - A wrong activation count or an unknown name is InvalidInput; surplus
  *     alpha/beta values are ignored.
  *   - The optional bf16 projection rounds X and W to bfloat16 (RNE) and then

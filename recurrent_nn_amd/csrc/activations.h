@@ -6,7 +6,7 @@
 // that a NaN argument gives what the written definition gives (NaN for all but
 // ThresholdedRelu, whose compare sends NaN to 0).  Sigmoid, Tanh and
 // ScaledTanh use the fast exp2-based forms below, Elu and Softplus the device
-// math library ("fast mode" on that page: fast elementwise functions).
+// math library (the fast mode of that page allows fast elementwise functions).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -110,7 +110,7 @@ struct ActAny {
     __device__ __forceinline__ float operator()(float x) const { return act_apply(s.kind, s.alpha, s.beta, x); }
 };
 
-// clip "when present and positive": clamp to [-c, c]; a NaN passes through.
+// clip, active only when given and positive: clamp to [-c, c]; a NaN passes through.
 __device__ __forceinline__ float clip_pre(float x, int on, float c)
 {
     if (!on)

@@ -333,7 +333,7 @@ extern "C" rnn_status rnn_plan_create(const rnn_attrs *attrs, const rnn_dims *di
     p->Bt = dims->batch_size;
     p->I = dims->input_size;
     p->H = dims->hidden;
-    p->clip_on = (a.has_clip && a.clip > 0.0f) ? 1 : 0;   // "when present and positive"
+    p->clip_on = (a.has_clip && a.clip > 0.0f) ? 1 : 0;   // only when given and positive
     p->clip = a.clip;
     p->input_forget = a.input_forget ? 1 : 0;
     p->lbr = a.linear_before_reset ? 1 : 0;

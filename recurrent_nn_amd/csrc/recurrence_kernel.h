@@ -33,7 +33,7 @@
 //
 // Epilogue.  This file is compiled with -ffp-contract=off: every written
 // addition and multiplication is its own IEEE operation, in the written order
-// ("No step fuses a multiply with an add").
+// (the page allows fused multiply-adds only inside the products).
 #pragma once
 
 #include <hip/hip_runtime.h>
