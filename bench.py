@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -63,7 +64,7 @@ def cpu_baseline(c, budget_s):
     first = time.perf_counter() - t0
     reps = 1
     if first < 10.0:
-        reps = max(1, min(int(10.0 / max(first, 1e-3)), int(budget_s / max(first, 1e-3))))
+        reps = max(1, min(math.ceil(10.0 / max(first, 1e-3)), int(budget_s / max(first, 1e-3))))
         t0 = time.perf_counter()
         for _ in range(reps):
             oracle.run(c, n_threads=nt, want_y=True)

@@ -99,6 +99,9 @@ typedef struct rnn_attrs {
     int32_t kernel_path;               /* rnn_kernel_path                                 */
     int32_t units_per_block;           /* 0 = automatic; hidden units per workgroup       */
     int32_t batch_tile;                /* 0 = automatic; batch rows per workgroup (16/32/64) */
+    int32_t waves_per_block;           /* 0 = automatic; 4 or 8 waves split the step product */
+    int32_t barrier_spin_limit;        /* 0 = default; polls before a step barrier gives up,
+                                          raising the error rnn_workspace_check reports   */
 } rnn_attrs;
 
 /* Dimensions: hidden is R's last dimension, num_directions W's first. */

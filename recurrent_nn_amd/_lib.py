@@ -46,6 +46,8 @@ class rnn_attrs(ctypes.Structure):
         ("kernel_path", ctypes.c_int32),
         ("units_per_block", ctypes.c_int32),
         ("batch_tile", ctypes.c_int32),
+        ("waves_per_block", ctypes.c_int32),
+        ("barrier_spin_limit", ctypes.c_int32),
     ]
 
 

@@ -27,10 +27,10 @@ struct ActSpec {
 // Stage indices for the optional event timing.
 enum Stage { STAGE_PACK = 0, STAGE_PROJ = 1, STAGE_REC = 2, STAGE_OTHER = 3, STAGE_COUNT = 4 };
 
-constexpr int kThreads = 256;          // threads per recurrence workgroup (4 waves)
-constexpr int kWaves = 4;
+constexpr int kThreads = 256;          // threads of the auxiliary kernels' workgroups
 constexpr int kMaxPairs = 8;           // (row, unit) pairs per thread in the epilogue
 constexpr int kMaxWorkgroups = 256;    // one workgroup per CU on MI355X
+constexpr uint32_t kDefaultSpinLimit = 1u << 26;   // ~seconds of polling: a step takes microseconds
 
 // Workspace layout: byte offsets from the workspace base, each 256-aligned.
 struct Layout {
@@ -63,6 +63,7 @@ struct rnn_plan {
     int32_t proj_bf16 = 0;
     int32_t constant_weights = 0;
     int32_t kernel_path = 0;
+    uint32_t spin_limit = 0;  // polls before a step barrier gives up
     int64_t S = 0, Bt = 0, I = 0, H = 0;
     rnnamd::ActSpec act[2][3] = {};
 
@@ -76,8 +77,9 @@ struct rnn_plan {
     int32_t NTB = 0;          // 16-column tiles of phase 1 (GRU lbr=0 candidate)
     int32_t NT = 1;           // NTA + NTB
     int32_t phases = 1;       // 2 for GRU lbr=0
-    int64_t Hp = 64;          // hidden padded to a multiple of 64 (K of the step product)
-    int32_t KB = 1;           // 16-wide k blocks per wave (Hp / 64)
+    int64_t Hp = 64;          // hidden padded to a multiple of 16 * NW (K of the step product)
+    int32_t NW = 4;           // waves per workgroup (4 or 8); they split k
+    int32_t KB = 1;           // 16-wide k blocks per wave (Hp / (16 * NW))
     int32_t resident = 0;     // R slice held in registers across steps
     int64_t Btp = 16;         // NBB * BT
     int32_t n_wg = 1;         // D * NBB * NUB
@@ -148,7 +150,7 @@ int launch_projection(const ProjArgs &a, void *stream);
 struct RecArgs {
     // sizes
     int32_t S, Bt, H, D, G, op;
-    int32_t Hp, KB, U, NUB, BT, NBB, MT, NTA, NTB, NT, phases;
+    int32_t Hp, KB, NW, U, NUB, BT, NBB, MT, NTA, NTB, NT, phases;
     int32_t Btp;
     int32_t reverse_only, layout, clip_on, input_forget, lbr;
     float clip;
@@ -167,7 +169,8 @@ struct RecArgs {
 // persistent: one cooperative launch covering every phase; else one phase.
 int launch_recurrence(const RecArgs &a, int resident, int persistent, void *stream);
 int recurrence_can_persist(const RecArgs &a, int resident, int device, int *ok);
-bool recurrence_supported(int mt, int nt, int nta, int phases, int kb, int bt, int u, int resident);
+bool recurrence_supported(int nw, int mt, int nt, int nta, int phases, int kb, int bt, int u,
+                          int resident);
 
 struct FinalArgs {
     const float *h0, *c0;

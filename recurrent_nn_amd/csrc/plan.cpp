@@ -136,16 +136,21 @@ void tiles_for(const rnn_plan &p, int uc, int *nta, int *ntb)
 // The recurrence kernel is compiled for these shapes only (recurrence.hip).
 // R in registers: 2 or 4 row tiles, 1 or 2 column tiles, 8 or 16 k blocks of
 // 16 per wave, at most 2 (row, unit) pairs per thread.
-bool resident_ok(int nt, int nta, int phases, int kb, int mt, int pairs)
+bool resident_ok(int nw, int nt, int nta, int phases, int kb, int mt, int pairs)
 {
     const bool tiles = phases == 1 ? nt <= 2 : (nt == 2 && nta == 1 && mt == 2);
-    return (mt == 2 || mt == 4) && tiles && (kb == 8 || kb == 16) && pairs <= 2;
+    // R slice per wave: nt * kb * 4 registers; 4 waves run one wave per SIMD
+    // (512 registers), 8 waves two (256 registers each)
+    const bool kbs = nw == 4 ? (kb == 8 || kb == 16) : (kb == 4 || kb == 8);
+    return (mt == 2 || mt == 4) && tiles && kbs && pairs <= 2;
 }
 
-// R streamed every step: 1, 2, 4 or 6 column tiles for one phase; for two
-// (GRU lbr=0) 1+1, 2+1 or 4+2; at most 8 pairs.
-bool streamed_ok(int nt, int nta, int phases, int pairs)
+// R streamed every step (4 waves): 1, 2, 4 or 6 column tiles for one phase;
+// for two (GRU lbr=0) 1+1, 2+1 or 4+2; at most 8 pairs.
+bool streamed_ok(int nw, int nt, int nta, int phases, int pairs)
 {
+    if (nw != 4)
+        return false;
     const bool tiles = phases == 1 ? (nt == 1 || nt == 2 || nt == 4 || nt == 6)
                                    : ((nt == 2 && nta == 1) || (nt == 3 && nta == 2) ||
                                       (nt == 6 && nta == 4));
@@ -168,9 +173,17 @@ rnn_status choose_tiling(const rnn_attrs &a, rnn_plan &p)
     p.MT = p.BT / 16;
     p.NBB = (int32_t)std::max<int64_t>(1, (p.Bt + p.BT - 1) / p.BT);
     p.Btp = (int64_t)p.NBB * p.BT;
-    p.Hp = round_up(std::max<int64_t>(p.H, 1), 64);
-    p.KB = (int32_t)(p.Hp / 64);
     p.phases = (p.op == RNN_OP_GRU && !p.lbr) ? 2 : 1;
+    if (a.waves_per_block != 0 && a.waves_per_block != 4 && a.waves_per_block != 8) {
+        set_error("waves_per_block must be 0, 4 or 8");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    auto set_waves = [&](int nw) {
+        p.NW = nw;
+        p.Hp = round_up(std::max<int64_t>(p.H, 1), 16 * nw);
+        p.KB = (int32_t)(p.Hp / (16 * nw));
+    };
+    set_waves(a.waves_per_block ? a.waves_per_block : 4);
 
     bool cap_wg = true;   // first look for tilings whose workgroups fit at once
     auto evaluate = [&](int u, int *nta, int *ntb, bool *res, long *cost) -> bool {
@@ -178,15 +191,16 @@ rnn_status choose_tiling(const rnn_attrs &a, rnn_plan &p)
         long wg = (long)p.D * p.NBB * nub;
         if (cap_wg && wg > kMaxWorkgroups && !a.units_per_block)
             return false;
-        if ((long)p.BT * u > (long)kThreads * kMaxPairs)
+        const int nthr = 64 * p.NW;
+        if ((long)p.BT * u > (long)nthr * kMaxPairs)
             return false;
         tiles_for(p, u, nta, ntb);
         int nt = *nta + *ntb;
-        int pairs = (p.BT * u + kThreads - 1) / kThreads;
-        *res = resident_ok(nt, *nta, p.phases, p.KB, p.MT, pairs);
-        if (!*res && !streamed_ok(nt, *nta, p.phases, pairs))
+        int pairs = (p.BT * u + nthr - 1) / nthr;
+        *res = resident_ok(p.NW, nt, *nta, p.phases, p.KB, p.MT, pairs);
+        if (!*res && !streamed_ok(p.NW, nt, *nta, p.phases, pairs))
             return false;
-        long lds = ((long)kWaves * p.BT * (nt * 16 + 4) + 3L * p.BT * u + p.BT + 11L * u) * 4;
+        long lds = ((long)p.NW * p.BT * (nt * 16 + 4) + 3L * p.BT * u + p.BT + 11L * u) * 4;
         if (lds > 160 * 1024)
             return false;
         *cost = (long)p.MT * nt * p.KB * 16 + (*res ? 0 : (long)p.MT * nt * p.KB * 4);
@@ -340,6 +354,9 @@ extern "C" rnn_status rnn_plan_create(const rnn_attrs *attrs, const rnn_dims *di
     p->proj_bf16 = a.proj_dtype == RNN_PROJ_BF16;
     p->constant_weights = a.constant_weights ? 1 : 0;
     p->kernel_path = a.kernel_path;
+    if (a.barrier_spin_limit < 0)
+        return fail(RNN_ERR_INVALID_INPUT, "barrier_spin_limit must be >= 0");
+    p->spin_limit = a.barrier_spin_limit ? (uint32_t)a.barrier_spin_limit : kDefaultSpinLimit;
 
     rnn_status st = resolve_activations(a, *p);
     if (st != RNN_OK)
@@ -383,11 +400,11 @@ extern "C" rnn_status rnn_plan_describe(const rnn_plan *p, char *buf, size_t len
     }
     std::snprintf(buf, len,
                   "op=%d G=%d D=%d S=%lld Bt=%lld I=%lld H=%lld U=%d NUB=%d BT=%d NBB=%d MT=%d "
-                  "NTA=%d NTB=%d phases=%d Hp=%lld KB=%d resident=%d workgroups=%d path=%d "
-                  "persist=%d ws=%zu",
+                  "NTA=%d NTB=%d phases=%d Hp=%lld waves=%d KB=%d resident=%d workgroups=%d "
+                  "path=%d persist=%d ws=%zu",
                   p->op, p->G, p->D, (long long)p->S, (long long)p->Bt, (long long)p->I,
                   (long long)p->H, p->U, p->NUB, p->BT, p->NBB, p->MT, p->NTA, p->NTB, p->phases,
-                  (long long)p->Hp, p->KB, p->resident, p->n_wg, p->kernel_path, p->can_persist,
-                  p->ws.total);
+                  (long long)p->Hp, p->NW, p->KB, p->resident, p->n_wg, p->kernel_path,
+                  p->can_persist, p->ws.total);
     return RNN_OK;
 }

@@ -8,17 +8,19 @@
 namespace rnnamd {
 
 #define RNN_DECL(A)                                                                               \
-    rec_fn rec_get_resident_a##A(int mt, int nt, int kb, int ta);                                 \
+    rec_fn rec_get_resident_a##A(int nw, int mt, int nt, int kb, int ta);                         \
     rec_fn rec_get_streamed2_a##A(int mt, int nt, int ta);                                        \
     rec_fn rec_get_streamed8_a##A(int mt, int nt, int ta);
 RNN_DECL(0)
 RNN_DECL(1)
 RNN_DECL(2)
 RNN_DECL(3)
+RNN_DECL(4)
 #undef RNN_DECL
 
-// Activation set compiled into the kernel: 1 Sigmoid/Tanh(/Tanh) for LSTM
-// and GRU, 2 HardSigmoid/Tanh for GRU, 3 Tanh for RNN, 0 anything else.
+// Operator and activation set compiled into the kernel: 1 LSTM with
+// Sigmoid/Tanh/Tanh, 2 GRU with HardSigmoid/Tanh, 3 RNN with Tanh, 4 GRU with
+// Sigmoid/Tanh, 0 anything else (run-time switch).
 static int act_set(const RecArgs &a)
 {
     bool same = true;                      // both directions use the same kinds
@@ -31,7 +33,7 @@ static int act_set(const RecArgs &a)
     if (a.op == RNN_OP_LSTM && f == ACT_SIGMOID && g == ACT_TANH && h == ACT_TANH)
         return 1;
     if (a.op == RNN_OP_GRU && f == ACT_SIGMOID && g == ACT_TANH)
-        return 1;
+        return 4;
     if (a.op == RNN_OP_GRU && f == ACT_HARDSIGMOID && g == ACT_TANH)
         return 2;
     if (a.op == RNN_OP_RNN && f == ACT_TANH)
@@ -39,13 +41,14 @@ static int act_set(const RecArgs &a)
     return 0;
 }
 
-static rec_fn get_resident(int act, int mt, int nt, int kb, int ta)
+static rec_fn get_resident(int act, int nw, int mt, int nt, int kb, int ta)
 {
     switch (act) {
-    case 1: return rec_get_resident_a1(mt, nt, kb, ta);
-    case 2: return rec_get_resident_a2(mt, nt, kb, ta);
-    case 3: return rec_get_resident_a3(mt, nt, kb, ta);
-    default: return rec_get_resident_a0(mt, nt, kb, ta);
+    case 1: return rec_get_resident_a1(nw, mt, nt, kb, ta);
+    case 2: return rec_get_resident_a2(nw, mt, nt, kb, ta);
+    case 3: return rec_get_resident_a3(nw, mt, nt, kb, ta);
+    case 4: return rec_get_resident_a4(nw, mt, nt, kb, ta);
+    default: return rec_get_resident_a0(nw, mt, nt, kb, ta);
     }
 }
 
@@ -55,17 +58,21 @@ static rec_fn get_streamed(int act, int p, int mt, int nt, int ta)
     case 1: return p == 2 ? rec_get_streamed2_a1(mt, nt, ta) : rec_get_streamed8_a1(mt, nt, ta);
     case 2: return p == 2 ? rec_get_streamed2_a2(mt, nt, ta) : rec_get_streamed8_a2(mt, nt, ta);
     case 3: return p == 2 ? rec_get_streamed2_a3(mt, nt, ta) : rec_get_streamed8_a3(mt, nt, ta);
+    case 4: return p == 2 ? rec_get_streamed2_a4(mt, nt, ta) : rec_get_streamed8_a4(mt, nt, ta);
     default: return p == 2 ? rec_get_streamed2_a0(mt, nt, ta) : rec_get_streamed8_a0(mt, nt, ta);
     }
 }
 
 static rec_fn pick(const RecArgs &a, int resident)
 {
-    const int np = (a.BT * a.U + kThreads - 1) / kThreads;
+    const int nthr = 64 * a.NW;
+    const int np = (a.BT * a.U + nthr - 1) / nthr;
     const int ta = a.phases == 2 ? a.NTA : 0;
     const int act = act_set(a);
     if (resident)
-        return np <= 2 ? get_resident(act, a.MT, a.NT, a.KB, ta) : nullptr;
+        return np <= 2 ? get_resident(act, a.NW, a.MT, a.NT, a.KB, ta) : nullptr;
+    if (a.NW != 4)
+        return nullptr;
     if (np <= 2)
         return get_streamed(act, 2, a.MT, a.NT, ta);
     if (np <= kMaxPairs)
@@ -73,9 +80,11 @@ static rec_fn pick(const RecArgs &a, int resident)
     return nullptr;
 }
 
-bool recurrence_supported(int mt, int nt, int nta, int phases, int kb, int bt, int u, int resident)
+bool recurrence_supported(int nw, int mt, int nt, int nta, int phases, int kb, int bt, int u,
+                          int resident)
 {
     RecArgs a{};
+    a.NW = nw;
     a.MT = mt;
     a.NT = nt;
     a.NTA = nta;
@@ -86,7 +95,7 @@ bool recurrence_supported(int mt, int nt, int nta, int phases, int kb, int bt, i
     return pick(a, resident) != nullptr;
 }
 
-static size_t rec_shmem(const RecArgs &a) { return rec_lds_bytes(a.BT, a.NT, a.U); }
+static size_t rec_shmem(const RecArgs &a) { return rec_lds_bytes(a.NW, a.BT, a.NT, a.U); }
 
 int recurrence_can_persist(const RecArgs &a, int resident, int device, int *ok)
 {
@@ -99,7 +108,7 @@ int recurrence_can_persist(const RecArgs &a, int resident, int device, int *ok)
     if (e != hipSuccess)
         return (int)e;
     int per_cu = 0, cus = 0, coop = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)f, kThreads,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)f, 64 * a.NW,
                                                      rec_shmem(a));
     if (e != hipSuccess)
         return (int)e;
@@ -128,11 +137,11 @@ int launch_recurrence(const RecArgs &a, int resident, int persistent, void *stre
     if (persistent) {
         RecArgs arg = a;
         void *params[] = {&arg};
-        e = hipLaunchCooperativeKernel((const void *)f, dim3(n_wg), dim3(kThreads), params,
+        e = hipLaunchCooperativeKernel((const void *)f, dim3(n_wg), dim3(64 * a.NW), params,
                                        (unsigned)shmem, (hipStream_t)stream);
         return (int)e;
     }
-    hipLaunchKernelGGL(f, dim3(n_wg), dim3(kThreads), shmem, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(f, dim3(n_wg), dim3(64 * a.NW), shmem, (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
 

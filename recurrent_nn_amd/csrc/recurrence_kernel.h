@@ -8,11 +8,11 @@
 //
 // Work split.  A workgroup owns (direction d, batch block bb of BT rows, unit
 // block ub of U hidden units) and computes every gate column of its units, so
-// the gate arithmetic of a unit never leaves the workgroup.  Its 4 waves split
-// the reduction index k of the product (Hp / 4 each) and compute the whole
-// [BT x 16*NT] tile over their k range with v_mfma_f32_16x16x4_f32; the four
-// partial tiles meet in LDS and are summed in a fixed order (w = 0, 1, 2, 3),
-// so the result does not depend on the grid size.  With `RES` the wave's
+// the gate arithmetic of a unit never leaves the workgroup.  Its NW (4 or 8)
+// waves split the reduction index k of the product (Hp / NW each) and compute
+// the whole [BT x 16*NT] tile over their k range with v_mfma_f32_16x16x4_f32;
+// the partial tiles meet in LDS and are summed in a fixed order (w = 0, 1,
+// ...), so the result does not depend on the grid size.  With `RES` the wave's
 // slice of R stays in registers for the whole sequence; otherwise it is
 // re-read (from L2 / the memory-side cache) every step.
 //
@@ -173,23 +173,24 @@ __device__ __forceinline__ void product_stream(f4 (&acc)[MT][NT], const float *a
 
 // LDS bytes of one workgroup: the four partial tiles, then the per-pair
 // states (h, c, z) and the per-row lengths.
-__host__ __device__ inline size_t rec_lds_bytes(int bt, int nt, int u)
+__host__ __device__ inline size_t rec_lds_bytes(int nw, int bt, int nt, int u)
 {
-    return ((size_t)kWaves * bt * (nt * 16 + 4) + 3 * (size_t)bt * u + bt + 11 * (size_t)u) * 4;
+    return ((size_t)nw * bt * (nt * 16 + 4) + 3 * (size_t)bt * u + bt + 11 * (size_t)u) * 4;
 }
 
 // Depth (in 16-k blocks) of the A-operand prefetch of the register-resident
 // product; deeper rings measured no faster and cost registers.
 constexpr int kPrefetch = 1;
 
-template <int MT, int NT, int KBR, int P, int TA, int ACT>
-__global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
+template <int MT, int NT, int KBR, int P, int TA, int ACT, int NW>
+__global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
 {
+    constexpr int kThreads = 64 * NW;            // NW waves split the k range
+    constexpr int kWaves = NW;
     constexpr bool RES = KBR > 0;
     constexpr int BT = MT * 16;
     constexpr int NTC = NT * 16;
     constexpr int LDR = NTC + 4;                 // LDS row stride of the partial tiles
-    constexpr bool kPrefetchXW = P <= 2;         // XW loads issued before the product
     extern __shared__ float smem[];
     float *red = smem;                           // [kWaves][BT][LDR] partial tiles
     float *hst = red + kWaves * BT * LDR;        // [BT * U] h of each (row, unit) pair
@@ -218,7 +219,10 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
     const int Hp = a.Hp;
     const bool rev = a.reverse_only || d == 1;
     const int GH = a.G * a.H;
-    const int op = a.op;
+    // ACT fixes the operator too: 1 LSTM, 2 and 4 GRU, 3 RNN; 0 reads it at run time
+    const int op = ACT == 1 ? (int)RNN_OP_LSTM
+                 : (ACT == 2 || ACT == 4) ? (int)RNN_OP_GRU
+                 : ACT == 3 ? (int)RNN_OP_RNN : a.op;
     const size_t plane = (size_t)a.D * a.Btp * Hp;           // one plane of the H history
     const size_t drow = ((size_t)d * a.Btp + row0) * Hp;     // this group's rows
     const int grp = d * a.NBB + bb;
@@ -256,6 +260,9 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
         }
         for (int rl = tid; rl < rows; rl += kThreads)
             lst[rl] = a.lens[row0 + rl];
+        // Wb, Rb (zeros when B is absent: adding +0 to a pre-activation is the
+        // identity here, since xw + rec is never -0 -- both sums start at +0),
+        // then the peepholes Pi, Po, Pf
         for (int e = tid; e < 11 * uc; e += kThreads) {
             const int k = e / uc, u = e - k * uc;
             float v = 0.0f;
@@ -270,6 +277,30 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
         __syncthreads();
     }
 
+    constexpr bool kPrefetchXW = P <= 2;
+    float xw_next[kPrefetchXW ? P : 1][4];
+    if constexpr (kPrefetchXW) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int pi = tid + kThreads * i;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                xw_next[i][g] = 0.0f;
+            if (pi < npairs && a.q_begin < a.q_end) {
+                const int jj = a.q_begin / a.phases, pp = a.q_begin - jj * a.phases;
+                const int rl = pi / uc, u = pi - rl * uc;
+                const int len = lst[rl];
+                if (jj < len) {
+                    const int t = rev ? len - 1 - jj : jj;
+                    const float *src = a.XW + xwd + ((size_t)t * a.Bt + row0 + rl) * GH + u;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        if (g < a.G && ((a.phases == 2 && pp == 1) ? g == 2 : !(a.phases == 2 && g == 2)))
+                            xw_next[i][g] = src[g * uc];
+                }
+            }
+        }
+    }
     bool dead = false;
     for (int q = a.q_begin; q < a.q_end; ++q) {
         const int j = q / a.phases;
@@ -278,16 +309,17 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
         const int t1 = ph == 0 ? a.NTA : a.NTA + a.NTB;
         const bool last_phase = ph == a.phases - 1;
 
-        // XW of pair pi at this step, gates of this phase (0 for inactive rows)
-        auto fetch_xw = [&](int pi, float *xv) {
+        // XW of pair pi for phase qq (0 for inactive rows)
+        auto fetch_xw_q = [&](int qq, int pi, float *xv) {
             xv[0] = xv[1] = xv[2] = xv[3] = 0.0f;
+            const int jj = qq / a.phases, pp = qq - jj * a.phases;
             const int rl = pi / uc, u = pi - rl * uc;
             const int len = lst[rl];
-            if (j >= len)
+            if (jj >= len)
                 return;
-            const int t = rev ? len - 1 - j : j;
+            const int t = rev ? len - 1 - jj : jj;
             const float *src = a.XW + xwd + ((size_t)t * a.Bt + row0 + rl) * GH + u;
-            if (a.phases == 2 && ph == 1) {
+            if (a.phases == 2 && pp == 1) {
                 xv[2] = src[2 * uc];
             } else {
 #pragma unroll
@@ -296,14 +328,27 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
                         xv[g] = src[g * uc];
             }
         };
+        auto fetch_xw = [&](int pi, float *xv) { fetch_xw_q(q, pi, xv); };
+        // With few pairs per thread the XW values of the NEXT phase are loaded
+        // during this one (issued after the product's last H load, so no
+        // product wait is held up by them); this phase uses last phase's.
         float xw[kPrefetchXW ? P : 1][4];
+        if constexpr (kPrefetchXW) {
+#pragma unroll
+            for (int i = 0; i < P; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    xw[i][g] = xw_next[i][g];
+        }
         auto prefetch_xw = [&]() {
             if constexpr (kPrefetchXW) {
+                if (q + 1 < a.q_end) {
 #pragma unroll
-                for (int i = 0; i < P; ++i) {
-                    const int pi = tid + kThreads * i;
-                    if (pi < npairs)
-                        fetch_xw(pi, xw[i]);
+                    for (int i = 0; i < P; ++i) {
+                        const int pi = tid + kThreads * i;
+                        if (pi < npairs)
+                            fetch_xw_q(q + 1, pi, xw_next[i]);
+                    }
                 }
             }
         };
@@ -344,13 +389,10 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
         __syncthreads();
         auto rec_at = [&](int rl, int col) {
             const float *p = red + rl * LDR + col;
-            float s0 = p[0];
-            float s1 = p[BT * LDR];
-            float s2 = p[2 * BT * LDR];
-            float s3 = p[3 * BT * LDR];
-            float v = s0 + s1;
-            v = v + s2;
-            v = v + s3;
+            float v = p[0];
+#pragma unroll
+            for (int w2 = 1; w2 < NW; ++w2)
+                v = v + p[w2 * BT * LDR];             // fixed wave order
             return v;
         };
 
@@ -368,33 +410,27 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
             if (active) {
                 if (op == RNN_OP_RNN) {
                     float pre = xv[0] + rec_at(rl, u);
-                    if (Wb) {
-                        pre = pre + cst_u[u];
-                        pre = pre + cst_u[4 * a.U + u];
-                    }
+                    pre = pre + cst_u[u];
+                    pre = pre + cst_u[4 * a.U + u];
                     pre = clip_pre(pre, a.clip_on, a.clip);
                     hn = F(pre);
                 } else if (op == RNN_OP_GRU) {
                     if (a.phases == 1) {                    // linear_before_reset = 1
                         float pz = xv[0] + rec_at(rl, u);
                         float pr = xv[1] + rec_at(rl, uc + u);
-                        if (Wb) {
-                            pz = pz + cst_u[u];
-                            pz = pz + cst_u[4 * a.U + u];
-                            pr = pr + cst_u[a.U + u];
-                            pr = pr + cst_u[5 * a.U + u];
-                        }
+                        pz = pz + cst_u[u];
+                        pz = pz + cst_u[4 * a.U + u];
+                        pr = pr + cst_u[a.U + u];
+                        pr = pr + cst_u[5 * a.U + u];
                         pz = clip_pre(pz, a.clip_on, a.clip);
                         pr = clip_pre(pr, a.clip_on, a.clip);
                         const float z = F(pz);
                         const float r = F(pr);
                         float rh = rec_at(rl, 2 * uc + u);
-                        if (Wb)
-                            rh = rh + cst_u[6 * a.U + u];
+                        rh = rh + cst_u[6 * a.U + u];
                         const float gated = r * rh;
                         float ph_ = xv[2] + gated;
-                        if (Wb)
-                            ph_ = ph_ + cst_u[2 * a.U + u];
+                        ph_ = ph_ + cst_u[2 * a.U + u];
                         ph_ = clip_pre(ph_, a.clip_on, a.clip);
                         const float ht = Gf(ph_);
                         const float omz = 1.0f - z;
@@ -404,12 +440,10 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
                     } else if (ph == 0) {                   // lbr = 0: z and r
                         float pz = xv[0] + rec_at(rl, u);
                         float pr = xv[1] + rec_at(rl, uc + u);
-                        if (Wb) {
-                            pz = pz + cst_u[u];
-                            pz = pz + cst_u[4 * a.U + u];
-                            pr = pr + cst_u[a.U + u];
-                            pr = pr + cst_u[5 * a.U + u];
-                        }
+                        pz = pz + cst_u[u];
+                        pz = pz + cst_u[4 * a.U + u];
+                        pr = pr + cst_u[a.U + u];
+                        pr = pr + cst_u[5 * a.U + u];
                         pz = clip_pre(pz, a.clip_on, a.clip);
                         pr = clip_pre(pr, a.clip_on, a.clip);
                         zst[pi] = F(pz);
@@ -417,10 +451,8 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
                         store_coherent(snext + (size_t)rl * Hp + gu, r * hp);   // r (.) H_prev
                     } else {                                // lbr = 0: candidate
                         float ph_ = xv[2] + rec_at(rl, a.NTA * 16 + u);
-                        if (Wb) {
-                            ph_ = ph_ + cst_u[2 * a.U + u];
-                            ph_ = ph_ + cst_u[6 * a.U + u];
-                        }
+                        ph_ = ph_ + cst_u[2 * a.U + u];
+                        ph_ = ph_ + cst_u[6 * a.U + u];
                         ph_ = clip_pre(ph_, a.clip_on, a.clip);
                         const float ht = Gf(ph_);
                         const float z = zst[pi];
@@ -434,10 +466,8 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         float v = xv[g] + rec_at(rl, g * uc + u);
-                        if (Wb) {
-                            v = v + cst_u[g * a.U + u];
-                            v = v + cst_u[(4 + g) * a.U + u];
-                        }
+                        v = v + cst_u[g * a.U + u];
+                        v = v + cst_u[(4 + g) * a.U + u];
                         pre[g] = v;
                     }
                     const float cp = cn;
@@ -501,9 +531,9 @@ __global__ void __launch_bounds__(kThreads, 1) rec_kernel(RecArgs a)
                 }
             }
         };
-        // ACT (compile time): 1 Sigmoid/Tanh/Tanh, 2 HardSigmoid/Tanh, 3 Tanh,
-        // 0 any set through the run-time switch
-        if constexpr (ACT == 1)
+        // ACT (compile time): 1 LSTM Sigmoid/Tanh/Tanh, 2 GRU HardSigmoid/Tanh,
+        // 3 RNN Tanh, 4 GRU Sigmoid/Tanh, 0 any set through the run-time switch
+        if constexpr (ACT == 1 || ACT == 4)
             run_pairs(ActSigmoid{}, ActTanh{}, ActTanh{});
         else if constexpr (ACT == 2)
             run_pairs(ActHardSigmoid{fa.alpha, fa.beta}, ActTanh{}, ActTanh{});

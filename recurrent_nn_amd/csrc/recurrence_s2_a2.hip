@@ -4,23 +4,23 @@
 
 namespace rnnamd {
 
-// R streamed every step, up to 2 (row, unit) pairs per thread.
+// R streamed every step (4 waves), up to 2 (row, unit) pairs per thread.
 rec_fn rec_get_streamed2_a2(int mt, int nt, int ta)
 {
 #define RNN_STR(MT_)                                                                              \
     if (mt == MT_) {                                                                             \
         if (ta == 0) {                                                                           \
             switch (nt) {                                                                        \
-            case 1: return rec_kernel<MT_, 1, 0, 2, 0, 2>;                                    \
-            case 2: return rec_kernel<MT_, 2, 0, 2, 0, 2>;                                    \
-            case 4: return rec_kernel<MT_, 4, 0, 2, 0, 2>;                                    \
-            case 6: return rec_kernel<MT_, 6, 0, 2, 0, 2>;                                    \
+            case 1: return rec_kernel<MT_, 1, 0, 2, 0, 2, 4>;                                 \
+            case 2: return rec_kernel<MT_, 2, 0, 2, 0, 2, 4>;                                 \
+            case 4: return rec_kernel<MT_, 4, 0, 2, 0, 2, 4>;                                 \
+            case 6: return rec_kernel<MT_, 6, 0, 2, 0, 2, 4>;                                 \
             default: return nullptr;                                                             \
             }                                                                                    \
         }                                                                                        \
-        if (nt == 2 && ta == 1) return rec_kernel<MT_, 2, 0, 2, 1, 2>;                        \
-        if (nt == 3 && ta == 2) return rec_kernel<MT_, 3, 0, 2, 2, 2>;                        \
-        if (nt == 6 && ta == 4) return rec_kernel<MT_, 6, 0, 2, 4, 2>;                        \
+        if (nt == 2 && ta == 1) return rec_kernel<MT_, 2, 0, 2, 1, 2, 4>;                     \
+        if (nt == 3 && ta == 2) return rec_kernel<MT_, 3, 0, 2, 2, 2, 4>;                     \
+        if (nt == 6 && ta == 4) return rec_kernel<MT_, 6, 0, 2, 4, 2, 4>;                     \
         return nullptr;                                                                          \
     }
     RNN_STR(1)

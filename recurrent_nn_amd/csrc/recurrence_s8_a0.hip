@@ -4,23 +4,23 @@
 
 namespace rnnamd {
 
-// R streamed every step, up to 8 (row, unit) pairs per thread.
+// R streamed every step (4 waves), up to 8 (row, unit) pairs per thread.
 rec_fn rec_get_streamed8_a0(int mt, int nt, int ta)
 {
 #define RNN_STR(MT_)                                                                              \
     if (mt == MT_) {                                                                             \
         if (ta == 0) {                                                                           \
             switch (nt) {                                                                        \
-            case 1: return rec_kernel<MT_, 1, 0, 8, 0, 0>;                                    \
-            case 2: return rec_kernel<MT_, 2, 0, 8, 0, 0>;                                    \
-            case 4: return rec_kernel<MT_, 4, 0, 8, 0, 0>;                                    \
-            case 6: return rec_kernel<MT_, 6, 0, 8, 0, 0>;                                    \
+            case 1: return rec_kernel<MT_, 1, 0, 8, 0, 0, 4>;                                 \
+            case 2: return rec_kernel<MT_, 2, 0, 8, 0, 0, 4>;                                 \
+            case 4: return rec_kernel<MT_, 4, 0, 8, 0, 0, 4>;                                 \
+            case 6: return rec_kernel<MT_, 6, 0, 8, 0, 0, 4>;                                 \
             default: return nullptr;                                                             \
             }                                                                                    \
         }                                                                                        \
-        if (nt == 2 && ta == 1) return rec_kernel<MT_, 2, 0, 8, 1, 0>;                        \
-        if (nt == 3 && ta == 2) return rec_kernel<MT_, 3, 0, 8, 2, 0>;                        \
-        if (nt == 6 && ta == 4) return rec_kernel<MT_, 6, 0, 8, 4, 0>;                        \
+        if (nt == 2 && ta == 1) return rec_kernel<MT_, 2, 0, 8, 1, 0, 4>;                     \
+        if (nt == 3 && ta == 2) return rec_kernel<MT_, 3, 0, 8, 2, 0, 4>;                     \
+        if (nt == 6 && ta == 4) return rec_kernel<MT_, 6, 0, 8, 4, 0, 4>;                     \
         return nullptr;                                                                          \
     }
     RNN_STR(1)

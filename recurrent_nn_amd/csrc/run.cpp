@@ -18,8 +18,6 @@ using namespace rnnamd;
 
 namespace {
 
-constexpr uint32_t kSpinLimit = 1u << 26;   // ~seconds of s_sleep: a barrier takes microseconds
-
 rnn_status hip_fail(hipError_t e, const char *where)
 {
     set_error(std::string(where) + ": " + hipGetErrorString(e));
@@ -55,6 +53,7 @@ RecArgs rec_args(const rnn_plan &p, unsigned char *ws, const float *B, const flo
     r.op = p.op;
     r.Hp = (int32_t)p.Hp;
     r.KB = p.KB;
+    r.NW = p.NW;
     r.U = p.U;
     r.NUB = p.NUB;
     r.BT = p.BT;
@@ -86,7 +85,7 @@ RecArgs rec_args(const rnn_plan &p, unsigned char *ws, const float *B, const flo
     r.Yc = Yc;
     r.bar = (uint32_t *)(ws + p.ws.bar);
     r.err = (int32_t *)(ws + p.ws.bar) + p.D * p.NBB * p.NUB;
-    r.spin_limit = kSpinLimit;
+    r.spin_limit = p.spin_limit;
     r.q_begin = 0;
     r.q_end = (int32_t)(p.S * p.phases);
     return r;

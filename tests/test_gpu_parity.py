@@ -326,3 +326,47 @@ def test_constant_weights_are_packed_once_and_reused():
     t = plan.last_timings()
     assert set(t) == set(ra.STAGES) and all(v >= 0 for v in t.values())
     compare(c, [to_np(x) for x in b])
+
+
+def test_eight_wave_product_matches_oracle():
+    c = workloads.random_case("LSTM", "bidirectional", 9, 40, 48, 512, seed=31, with_lens=True,
+                              with_h0=True, with_c0=True, scale=1.5 / 512 ** 0.5)
+    say(f"case {c.name} with 8 waves")
+    plan = ra.plan_for_case(c, waves_per_block=8)
+    assert "waves=8" in plan.describe() and "resident=1" in plan.describe()
+    compare(c, run_gpu(c, waves_per_block=8))
+
+
+@pytest.mark.parametrize("op,attrs", [("LSTM", {}), ("GRU", dict(linear_before_reset=1)),
+                                      ("GRU", dict(linear_before_reset=0)), ("RNN", {})])
+def test_resident_kernels_without_bias_match_oracle(op, attrs):
+    # H = 512 takes the register-resident kernels; B absent is staged as zeros
+    c = workloads.random_case(op, "forward", 6, 32, 40, 512, seed=41, with_bias=False,
+                              with_lens=True, with_h0=True, with_c0=(op == "LSTM"),
+                              scale=1.5 / 512 ** 0.5, **attrs)
+    say(f"case {c.name} {attrs}")
+    assert "resident=1" in ra.plan_for_case(c).describe()
+    compare(c, run_gpu(c))
+
+
+def test_a_stalled_barrier_raises_the_device_error_and_the_kernel_exits():
+    # A spin limit of 1 lets each step barrier poll twice before it gives up:
+    # with 256 co-resident workgroups their arrival skew alone exceeds that,
+    # so a barrier times out; the kernel then runs on without waiting and
+    # exits normally, and rnn_workspace_check reports the error it raised.
+    c = workloads.random_case("LSTM", "bidirectional", 8, 64, 16, 1024, seed=3, with_h0=True,
+                              scale=1.0 / 32)
+    say(f"case {c.name} with barrier_spin_limit=1")
+    plan = ra.plan_for_case(c, kernel_path=ra.RNN_PATH_PERSISTENT, barrier_spin_limit=1)
+    assert "workgroups=256" in plan.describe()
+    ra.run_case(c, plan=plan)
+    torch.cuda.synchronize()
+    with pytest.raises(ra.RNNError) as ei:
+        plan.check()
+    assert ei.value.status == ra.RNN_ERR_DEVICE
+    # the default limit on the same inputs is clean and matches the oracle
+    plan2 = ra.plan_for_case(c, kernel_path=ra.RNN_PATH_PERSISTENT)
+    out = ra.run_case(c, plan=plan2)
+    torch.cuda.synchronize()
+    plan2.check()
+    compare(c, [to_np(x) for x in out])
