@@ -39,7 +39,113 @@ def parse():
     p.add_argument("--kernel-path", type=int, default=0, help="0 auto, 1 persistent, 2 per step")
     p.add_argument("--cpu-budget-s", type=float, default=30.0, help="0 skips the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB -> 1 GiB device copy kernel (to scale HBM counters)")
+    p.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                          "COPY_WRITE_DIR"),
+                   help="summarise four rocprofv3 --pmc csv runs (FETCH_SIZE / WRITE_SIZE of the "
+                        "bench and of --copy-calibration) into per-launch HBM bytes, as JSON")
     return p.parse_args()
+
+
+# Source files whose kernels a traffic figure was measured on; a figure whose
+# hash no longer matches the tree is stale and not reported.
+KERNEL_SOURCES = {
+    "recurrence": ["recurrence_kernel.h", "activations.h", "common.h", "recurrence.hip"],
+    "projection": ["proj_gemm.hip", "common.h"],
+}
+KERNEL_NAMES = {"recurrence": "rec_kernel", "projection": "proj_gemm"}
+COPY_BYTES = 1 << 30
+
+
+def kernel_hash(stage):
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "recurrent_nn_amd", "csrc")
+    names = list(KERNEL_SOURCES[stage])
+    if stage == "recurrence":
+        names += sorted(f for f in os.listdir(csrc) if f.startswith("recurrence_") and f.endswith(".hip"))
+    for n in names:
+        with open(os.path.join(csrc, n), "rb") as f:
+            h.update(n.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration():
+    """A plain elementwise copy (negation) of COPY_BYTES into COPY_BYTES: the
+    reference for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES}), flush=True)
+
+
+def _pmc_rows(d):
+    """(kernel name, dispatch id, counter value) from every rocprofv3 counter
+    csv below directory d."""
+    import csv
+    import glob
+    rows = []
+    for fn in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                rows.append((r["Kernel_Name"], int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return rows
+
+
+def traffic_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, workload):
+    """Per-launch HBM bytes of each kernel: mean counter KiB per dispatch,
+    scaled by bytes / counter of the plain copy."""
+    import numpy as np
+
+    def per_kernel(d):
+        acc = {}
+        for name, did, v in _pmc_rows(d):
+            acc.setdefault(name, {}).setdefault(did, 0.0)
+            acc[name][did] += v
+        return {k: float(np.mean(list(v.values()))) for k, v in acc.items()}
+
+    def copy_kib(d):
+        pk = per_kernel(d)
+        name = max(pk, key=pk.get)
+        return name, pk[name]
+
+    cname, cf = copy_kib(cfetch_dir)
+    _, cw = copy_kib(cwrite_dir)
+    rscale, wscale = COPY_BYTES / (cf * 1024.0), COPY_BYTES / (cw * 1024.0)
+    fk, wk = per_kernel(fetch_dir), per_kernel(write_dir)
+    out = {"workload": workload, "copy_kernel": cname, "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "read_scale": rscale, "write_scale": wscale, "kernels": {}}
+    for stage, prefix in KERNEL_NAMES.items():
+        names = [n for n in fk if prefix in n]
+        if not names:
+            continue
+        n = max(names, key=fk.get)
+        f_kib, w_kib = fk[n], wk.get(n, float("nan"))
+        out["kernels"][stage] = {
+            "name": n, "fetch_kib": f_kib, "write_kib": w_kib,
+            "traffic_bytes": f_kib * 1024.0 * rscale + w_kib * 1024.0 * wscale,
+            "source_hash": kernel_hash(stage)}
+    print(json.dumps(out, indent=1))
+
+
+def measured_traffic(workload, stage):
+    """Bytes per launch recorded for this kernel and workload, or None when
+    absent or taken on different kernel sources."""
+    fn = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    try:
+        with open(fn) as f:
+            k = json.load(f)["kernels"][stage]
+    except (OSError, KeyError, ValueError):
+        return None
+    if k.get("source_hash") != kernel_hash(stage):
+        return None
+    return k["traffic_bytes"]
 
 
 def flops_per_run(c):
@@ -79,6 +185,9 @@ def cpu_baseline(c, budget_s):
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary, workload=args.workload)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -91,6 +200,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     ra._lib.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -158,7 +270,8 @@ def main():
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
     dk = kernels[dom]
     roofline = {"bound": dk["bound"], "achieved": round(dk["achieved"], 3), "peak": dk["peak"],
-                "unit": dk["unit"], "frac": round(dk["frac"], 4), "traffic": None,
+                "unit": dk["unit"], "frac": round(dk["frac"], 4),
+                "traffic": measured_traffic(c.name, dom),
                 "kernel": dom}
 
     cells = c.cell_updates()
