@@ -51,10 +51,10 @@ def parse():
 # Source files whose kernels a traffic figure was measured on; a figure whose
 # hash no longer matches the tree is stale and not reported.
 KERNEL_SOURCES = {
-    "recurrence": ["recurrence_kernel.h", "activations.h", "common.h", "recurrence.hip"],
+    "recurrence": ["activations.h", "common.h"],     # + every recurrence* file
     "projection": ["proj_gemm.hip", "common.h"],
 }
-KERNEL_NAMES = {"recurrence": "rec_kernel", "projection": "proj_gemm"}
+KERNEL_NAMES = {"recurrence": "rec_", "projection": "proj_gemm"}
 COPY_BYTES = 1 << 30
 
 
@@ -64,7 +64,7 @@ def kernel_hash(stage):
     csrc = os.path.join(ROOT, "recurrent_nn_amd", "csrc")
     names = list(KERNEL_SOURCES[stage])
     if stage == "recurrence":
-        names += sorted(f for f in os.listdir(csrc) if f.startswith("recurrence_") and f.endswith(".hip"))
+        names += sorted(f for f in os.listdir(csrc) if f.startswith("recurrence"))
     for n in names:
         with open(os.path.join(csrc, n), "rb") as f:
             h.update(n.encode() + b"\0" + f.read())

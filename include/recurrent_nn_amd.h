@@ -102,6 +102,13 @@ typedef struct rnn_attrs {
     int32_t waves_per_block;           /* 0 = automatic; 4 or 8 waves split the step product */
     int32_t barrier_spin_limit;        /* 0 = default; polls before a step barrier gives up,
                                           raising the error rnn_workspace_check reports   */
+    int32_t batch_halves;              /* 0 = automatic; 1 = each step over the whole batch
+                                          tile; 2 = each step as two half-tile sub-steps, so
+                                          that one half's H exchange overlaps the other
+                                          half's product (needs R resident in registers, an
+                                          RNN, LSTM or GRU with linear_before_reset = 1, and
+                                          a batch tile of 32 or 64; else InvalidInput).
+                                          Results are identical either way.              */
 } rnn_attrs;
 
 /* Dimensions: hidden is R's last dimension, num_directions W's first. */
@@ -160,7 +167,11 @@ rnn_status rnn_run(rnn_plan *plan, void *hip_stream, void *workspace, size_t wor
 /*
  * rnn_workspace_check -- wait for `hip_stream`, then read the device-side
  * error word that the last run on this workspace left (a step barrier that
- * timed out).  RNN_OK when clean, RNN_ERR_DEVICE otherwise.
+ * timed out).  RNN_OK when clean, RNN_ERR_DEVICE otherwise.  For tests of
+ * this path, a plan created while the environment variable
+ * RNN_AMD_TEST_WITHHOLD_FLAGS is set to a non-zero value never stores its
+ * step flags, so every wait between steps runs out barrier_spin_limit (results
+ * are then undefined, and the kernel still finishes).
  */
 rnn_status rnn_workspace_check(const rnn_plan *plan, void *hip_stream, const void *workspace);
 

@@ -104,7 +104,7 @@ def make_attrs(op: str, direction: str = "forward", hidden_size: int = 0, layout
                input_forget: int = 0, linear_before_reset: int = 0, proj_bf16: bool = False,
                constant_weights: bool = False, kernel_path: int = RNN_PATH_AUTO,
                units_per_block: int = 0, batch_tile: int = 0, waves_per_block: int = 0,
-               barrier_spin_limit: int = 0):
+               barrier_spin_limit: int = 0, batch_halves: int = 0):
     """Returns (attrs, keepalive); keep `keepalive` alive while attrs is used."""
     keep = []
     a = rnn_attrs()
@@ -139,6 +139,7 @@ def make_attrs(op: str, direction: str = "forward", hidden_size: int = 0, layout
     a.batch_tile = batch_tile
     a.waves_per_block = waves_per_block
     a.barrier_spin_limit = barrier_spin_limit
+    a.batch_halves = batch_halves
     return a, keep
 
 

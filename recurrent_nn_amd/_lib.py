@@ -48,6 +48,7 @@ class rnn_attrs(ctypes.Structure):
         ("batch_tile", ctypes.c_int32),
         ("waves_per_block", ctypes.c_int32),
         ("barrier_spin_limit", ctypes.c_int32),
+        ("batch_halves", ctypes.c_int32),
     ]
 
 

@@ -43,7 +43,7 @@ struct Layout {
     size_t cbuf = 0;    // LSTM cell state between launches [D][Bt][H]
     size_t zbuf = 0;    // GRU lbr=0 update gate between launches [D][Bt][H]
     size_t lens = 0;    // int32 [Bt]
-    size_t bar = 0;     // uint32 step flags [D*NBB*NUB], then int32 error word
+    size_t bar = 0;     // uint32 step flags [D*NBB][2][NUB], then int32 error word
     size_t total = 0;
 };
 
@@ -64,6 +64,7 @@ struct rnn_plan {
     int32_t constant_weights = 0;
     int32_t kernel_path = 0;
     uint32_t spin_limit = 0;  // polls before a step barrier gives up
+    int32_t withhold_flags = 0;   // test fault injection: step flags are never stored
     int64_t S = 0, Bt = 0, I = 0, H = 0;
     rnnamd::ActSpec act[2][3] = {};
 
@@ -81,6 +82,7 @@ struct rnn_plan {
     int32_t NW = 4;           // waves per workgroup (4 or 8); they split k
     int32_t KB = 1;           // 16-wide k blocks per wave (Hp / (16 * NW))
     int32_t resident = 0;     // R slice held in registers across steps
+    int32_t halves = 1;       // 2: each step as two half-batch sub-steps (rec_pipe_kernel)
     int64_t Btp = 16;         // NBB * BT
     int32_t n_wg = 1;         // D * NBB * NUB
 
@@ -105,6 +107,8 @@ struct rnn_plan {
 namespace rnnamd {
 
 void set_error(const std::string &msg);
+// step flags in the workspace: one per (direction, batch block, half, unit block)
+inline int64_t n_flags(const rnn_plan &p) { return (int64_t)p.D * p.NBB * 2 * p.NUB; }
 int64_t round_up(int64_t x, int64_t m);
 void block_columns(const rnn_plan &p, int64_t ub, int32_t *u0, int32_t *uc);
 
@@ -130,7 +134,7 @@ struct InitArgs {
     int32_t *lens_dev;
     int32_t fill_lens;          // >= 0: every row gets this length (sequence_lens absent)
     uint32_t *bar;
-    int32_t n_bar;
+    int64_t n_bar;
     int64_t D, Bt, Btp, H, Hp;
     int32_t layout;
 };
@@ -152,6 +156,7 @@ struct RecArgs {
     int32_t S, Bt, H, D, G, op;
     int32_t Hp, KB, NW, U, NUB, BT, NBB, MT, NTA, NTB, NT, phases;
     int32_t Btp;
+    int32_t halves;         // 1, or 2 half-batch sub-steps per step (rec_pipe_kernel)
     int32_t reverse_only, layout, clip_on, input_forget, lbr;
     float clip;
     ActSpec act[2][3];
@@ -163,6 +168,7 @@ struct RecArgs {
     uint32_t *bar;
     int32_t *err;
     uint32_t spin_limit;
+    int32_t withhold_flags;  // test fault injection: never store the step flags
     // launch range in phase units (step j, phase p) -> q = j * phases + p
     int32_t q_begin, q_end;
 };
@@ -170,7 +176,7 @@ struct RecArgs {
 int launch_recurrence(const RecArgs &a, int resident, int persistent, void *stream);
 int recurrence_can_persist(const RecArgs &a, int resident, int device, int *ok);
 bool recurrence_supported(int nw, int mt, int nt, int nta, int phases, int kb, int bt, int u,
-                          int resident);
+                          int resident, int halves);
 
 struct FinalArgs {
     const float *h0, *c0;

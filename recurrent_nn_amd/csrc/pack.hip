@@ -173,8 +173,8 @@ __global__ void init_kernel(InitArgs a)
     if (a.fill_lens >= 0)
         for (int64_t b = tid; b < a.Bt; b += stride)
             a.lens_dev[b] = a.fill_lens;
-    if (tid <= a.n_bar)
-        a.bar[tid] = 0u;        // counters, then the error word
+    for (int64_t i = tid; i <= a.n_bar; i += stride)
+        a.bar[i] = 0u;          // step flags, then the error word
 }
 
 int launch_init(const InitArgs &a, void *stream)

@@ -8,6 +8,7 @@
 #include <cctype>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -254,6 +255,21 @@ rnn_status choose_tiling(const rnn_attrs &a, rnn_plan &p)
     p.NT = bnta + bntb;
     p.resident = bres ? 1 : 0;
     p.n_wg = p.D * p.NBB * p.NUB;
+
+    // Two half-batch sub-steps per step (rec_pipe_kernel): R resident, four
+    // waves, one phase per step, at most two pairs per thread and half.
+    const bool halves_ok = p.resident && p.NW == 4 && p.phases == 1 && (p.MT == 2 || p.MT == 4) &&
+                           p.NT <= 2 && (p.KB == 8 || p.KB == 16) &&
+                           (long)(p.BT / 2) * p.U <= 2L * 256;
+    if (a.batch_halves < 0 || a.batch_halves > 2) {
+        set_error("batch_halves must be 0, 1 or 2");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    if (a.batch_halves == 2 && !halves_ok) {
+        set_error("batch_halves = 2 needs R resident, a single-phase operator and a batch tile of 32 or 64");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    p.halves = (halves_ok && a.batch_halves != 1) ? 2 : 1;
     return RNN_OK;
 }
 
@@ -277,7 +293,7 @@ void make_layout(rnn_plan &p)
     L.cbuf = take(p.op == RNN_OP_LSTM ? (size_t)p.D * p.Bt * p.H * 4 : 0);
     L.zbuf = take(p.phases == 2 ? (size_t)p.D * p.Bt * p.H * 4 : 0);
     L.lens = take((size_t)std::max<int64_t>(p.Bt, 1) * 4);
-    L.bar = take((size_t)(p.D * p.NBB * p.NUB + 1) * 4);
+    L.bar = take((size_t)(n_flags(p) + 1) * 4);
     L.total = off;
 }
 
@@ -357,6 +373,13 @@ extern "C" rnn_status rnn_plan_create(const rnn_attrs *attrs, const rnn_dims *di
     if (a.barrier_spin_limit < 0)
         return fail(RNN_ERR_INVALID_INPUT, "barrier_spin_limit must be >= 0");
     p->spin_limit = a.barrier_spin_limit ? (uint32_t)a.barrier_spin_limit : kDefaultSpinLimit;
+    // Fault injection for tests of the barrier time-out: with this set, the
+    // step loops never store their flags, so every wait between steps runs
+    // out its (bounded) spin limit and the kernel then finishes normally.
+    {
+        const char *e = std::getenv("RNN_AMD_TEST_WITHHOLD_FLAGS");
+        p->withhold_flags = (e && *e && *e != '0') ? 1 : 0;
+    }
 
     rnn_status st = resolve_activations(a, *p);
     if (st != RNN_OK)
@@ -400,11 +423,11 @@ extern "C" rnn_status rnn_plan_describe(const rnn_plan *p, char *buf, size_t len
     }
     std::snprintf(buf, len,
                   "op=%d G=%d D=%d S=%lld Bt=%lld I=%lld H=%lld U=%d NUB=%d BT=%d NBB=%d MT=%d "
-                  "NTA=%d NTB=%d phases=%d Hp=%lld waves=%d KB=%d resident=%d workgroups=%d "
+                  "NTA=%d NTB=%d phases=%d Hp=%lld waves=%d KB=%d resident=%d halves=%d workgroups=%d "
                   "path=%d persist=%d ws=%zu",
                   p->op, p->G, p->D, (long long)p->S, (long long)p->Bt, (long long)p->I,
                   (long long)p->H, p->U, p->NUB, p->BT, p->NBB, p->MT, p->NTA, p->NTB, p->phases,
-                  (long long)p->Hp, p->NW, p->KB, p->resident, p->n_wg, p->kernel_path,
+                  (long long)p->Hp, p->NW, p->KB, p->resident, p->halves, p->n_wg, p->kernel_path,
                   p->can_persist, p->ws.total);
     return RNN_OK;
 }

@@ -3,14 +3,15 @@
 // persistent (cooperative) form, and the launches.
 #include <hip/hip_runtime.h>
 
-#include "recurrence_kernel.h"
+#include "recurrence_pipe.h"
 
 namespace rnnamd {
 
 #define RNN_DECL(A)                                                                               \
     rec_fn rec_get_resident_a##A(int nw, int mt, int nt, int kb, int ta);                         \
     rec_fn rec_get_streamed2_a##A(int mt, int nt, int ta);                                        \
-    rec_fn rec_get_streamed8_a##A(int mt, int nt, int ta);
+    rec_fn rec_get_streamed8_a##A(int mt, int nt, int ta);                                        \
+    rec_fn rec_get_pipe_a##A(int mth, int nt, int kb);
 RNN_DECL(0)
 RNN_DECL(1)
 RNN_DECL(2)
@@ -63,8 +64,26 @@ static rec_fn get_streamed(int act, int p, int mt, int nt, int ta)
     }
 }
 
+static rec_fn get_pipe(int act, int mth, int nt, int kb)
+{
+    switch (act) {
+    case 1: return rec_get_pipe_a1(mth, nt, kb);
+    case 2: return rec_get_pipe_a2(mth, nt, kb);
+    case 3: return rec_get_pipe_a3(mth, nt, kb);
+    case 4: return rec_get_pipe_a4(mth, nt, kb);
+    default: return rec_get_pipe_a0(mth, nt, kb);
+    }
+}
+
 static rec_fn pick(const RecArgs &a, int resident)
 {
+    if (a.halves == 2) {
+        // two half-batch sub-steps per step: R in registers, four waves, one
+        // phase, at most two pairs per thread and half
+        const bool ok = resident && a.NW == 4 && a.phases == 1 && a.MT % 2 == 0 &&
+                        (a.BT / 2) * a.U <= 2 * 256;
+        return ok ? get_pipe(act_set(a), a.MT / 2, a.NT, a.KB) : nullptr;
+    }
     const int nthr = 64 * a.NW;
     const int np = (a.BT * a.U + nthr - 1) / nthr;
     const int ta = a.phases == 2 ? a.NTA : 0;
@@ -81,9 +100,10 @@ static rec_fn pick(const RecArgs &a, int resident)
 }
 
 bool recurrence_supported(int nw, int mt, int nt, int nta, int phases, int kb, int bt, int u,
-                          int resident)
+                          int resident, int halves)
 {
     RecArgs a{};
+    a.halves = halves;
     a.NW = nw;
     a.MT = mt;
     a.NT = nt;
@@ -95,7 +115,12 @@ bool recurrence_supported(int nw, int mt, int nt, int nta, int phases, int kb, i
     return pick(a, resident) != nullptr;
 }
 
-static size_t rec_shmem(const RecArgs &a) { return rec_lds_bytes(a.NW, a.BT, a.NT, a.U); }
+static size_t rec_shmem(const RecArgs &a)
+{
+    return a.halves == 2 ? rec_pipe_lds_bytes(a.BT, a.NT, a.U) : rec_lds_bytes(a.NW, a.BT, a.NT, a.U);
+}
+
+static int rec_threads(const RecArgs &a) { return 64 * a.NW; }
 
 int recurrence_can_persist(const RecArgs &a, int resident, int device, int *ok)
 {
@@ -108,7 +133,7 @@ int recurrence_can_persist(const RecArgs &a, int resident, int device, int *ok)
     if (e != hipSuccess)
         return (int)e;
     int per_cu = 0, cus = 0, coop = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)f, 64 * a.NW,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)f, rec_threads(a),
                                                      rec_shmem(a));
     if (e != hipSuccess)
         return (int)e;
@@ -137,11 +162,11 @@ int launch_recurrence(const RecArgs &a, int resident, int persistent, void *stre
     if (persistent) {
         RecArgs arg = a;
         void *params[] = {&arg};
-        e = hipLaunchCooperativeKernel((const void *)f, dim3(n_wg), dim3(64 * a.NW), params,
+        e = hipLaunchCooperativeKernel((const void *)f, dim3(n_wg), dim3(rec_threads(a)), params,
                                        (unsigned)shmem, (hipStream_t)stream);
         return (int)e;
     }
-    hipLaunchKernelGGL(f, dim3(n_wg), dim3(64 * a.NW), shmem, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(f, dim3(n_wg), dim3(rec_threads(a)), shmem, (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
 

@@ -59,13 +59,15 @@ __device__ __forceinline__ void store_coherent(float *p, float v)
 // coherent stores have completed, then one wave polls the group's flags.
 // No whole-cache writeback or invalidate is needed: every step writes a
 // fresh plane of the H history that no cache has seen before.  A wait longer
-// than spin_limit polls raises the error word and stops waiting.
+// than spin_limit polls raises the error word and stops waiting.  `withhold`
+// (test fault injection) skips the flag store.
 __device__ __forceinline__ void group_barrier(uint32_t *flags, int nub, int me, uint32_t target,
-                                              int32_t *err, uint32_t spin_limit, bool &dead)
+                                              int32_t *err, uint32_t spin_limit, bool withhold,
+                                              bool &dead)
 {
     wait_stores();                 // this wave's coherent stores have completed
     __syncthreads();
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0 && !withhold)
         __hip_atomic_store(flags + me, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (threadIdx.x < 64 && !dead) {
         uint32_t n = 0;
@@ -169,6 +171,83 @@ __device__ __forceinline__ void product_stream(f4 (&acc)[MT][NT], const float *a
                 bv[nt] = bn[nt];
         }
     }
+}
+
+// Gate arithmetic of one (row, unit) pair for the single-phase operators (RNN,
+// GRU with linear_before_reset = 1, LSTM), in the written order.  xv[g] is the
+// pair's XW value of gate g, rec(g) its recurrent product, cu the staged
+// per-unit constants ([11][U]: Wb and Rb per gate, then Pi, Po, Pf), hp the
+// previous h and c the LSTM cell state (updated in place).  Returns the new h.
+template <typename F, typename Gf, typename Hf, typename Rec>
+__device__ __forceinline__ float gates_one_phase(int op, const float *xv, Rec rec, const float *cu,
+                                                 int U, int u, bool peep, bool clip_on, float clip,
+                                                 bool input_forget, float hp, float &c, F f, Gf g,
+                                                 Hf h)
+{
+    if (op == RNN_OP_RNN) {
+        float pre = xv[0] + rec(0);
+        pre = pre + cu[u];
+        pre = pre + cu[4 * U + u];
+        pre = clip_pre(pre, clip_on, clip);
+        return f(pre);
+    }
+    if (op == RNN_OP_GRU) {                                 // linear_before_reset = 1
+        float pz = xv[0] + rec(0);
+        float pr = xv[1] + rec(1);
+        pz = pz + cu[u];
+        pz = pz + cu[4 * U + u];
+        pr = pr + cu[U + u];
+        pr = pr + cu[5 * U + u];
+        pz = clip_pre(pz, clip_on, clip);
+        pr = clip_pre(pr, clip_on, clip);
+        const float z = f(pz);
+        const float r = f(pr);
+        float rh = rec(2);
+        rh = rh + cu[6 * U + u];
+        const float gated = r * rh;
+        float ph = xv[2] + gated;
+        ph = ph + cu[2 * U + u];
+        ph = clip_pre(ph, clip_on, clip);
+        const float ht = g(ph);
+        const float omz = 1.0f - z;
+        const float a1 = omz * ht;
+        const float a2 = z * hp;
+        return a1 + a2;
+    }
+    // LSTM: i, o, f, c
+    float pre[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float v = xv[k] + rec(k);
+        v = v + cu[k * U + u];
+        v = v + cu[(4 + k) * U + u];
+        pre[k] = v;
+    }
+    const float cp = c;
+    if (peep) {
+        const float pi_ = cu[8 * U + u] * cp;
+        const float pf_ = cu[10 * U + u] * cp;
+        pre[0] = pre[0] + pi_;
+        pre[2] = pre[2] + pf_;
+    }
+    const float ci = clip_pre(pre[0], clip_on, clip);
+    const float cf = clip_pre(pre[2], clip_on, clip);
+    const float cc = clip_pre(pre[3], clip_on, clip);
+    const float ig = f(ci);
+    const float fg = input_forget ? 1.0f - ig : f(cf);
+    const float ct = g(cc);
+    const float k1 = fg * cp;
+    const float k2 = ig * ct;
+    c = k1 + k2;
+    float po = pre[1];
+    if (peep) {
+        const float pov = cu[9 * U + u] * c;
+        po = po + pov;
+    }
+    po = clip_pre(po, clip_on, clip);
+    const float og = f(po);
+    const float hc = h(c);
+    return og * hc;
 }
 
 // LDS bytes of one workgroup: the four partial tiles, then the per-pair
@@ -408,94 +487,33 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
             const float hp = hst[pi];
             float hn = hp, cn = cst[pi];
             if (active) {
-                if (op == RNN_OP_RNN) {
-                    float pre = xv[0] + rec_at(rl, u);
-                    pre = pre + cst_u[u];
-                    pre = pre + cst_u[4 * a.U + u];
-                    pre = clip_pre(pre, a.clip_on, a.clip);
-                    hn = F(pre);
-                } else if (op == RNN_OP_GRU) {
-                    if (a.phases == 1) {                    // linear_before_reset = 1
-                        float pz = xv[0] + rec_at(rl, u);
-                        float pr = xv[1] + rec_at(rl, uc + u);
-                        pz = pz + cst_u[u];
-                        pz = pz + cst_u[4 * a.U + u];
-                        pr = pr + cst_u[a.U + u];
-                        pr = pr + cst_u[5 * a.U + u];
-                        pz = clip_pre(pz, a.clip_on, a.clip);
-                        pr = clip_pre(pr, a.clip_on, a.clip);
-                        const float z = F(pz);
-                        const float r = F(pr);
-                        float rh = rec_at(rl, 2 * uc + u);
-                        rh = rh + cst_u[6 * a.U + u];
-                        const float gated = r * rh;
-                        float ph_ = xv[2] + gated;
-                        ph_ = ph_ + cst_u[2 * a.U + u];
-                        ph_ = clip_pre(ph_, a.clip_on, a.clip);
-                        const float ht = Gf(ph_);
-                        const float omz = 1.0f - z;
-                        const float a1 = omz * ht;
-                        const float a2 = z * hp;
-                        hn = a1 + a2;
-                    } else if (ph == 0) {                   // lbr = 0: z and r
-                        float pz = xv[0] + rec_at(rl, u);
-                        float pr = xv[1] + rec_at(rl, uc + u);
-                        pz = pz + cst_u[u];
-                        pz = pz + cst_u[4 * a.U + u];
-                        pr = pr + cst_u[a.U + u];
-                        pr = pr + cst_u[5 * a.U + u];
-                        pz = clip_pre(pz, a.clip_on, a.clip);
-                        pr = clip_pre(pr, a.clip_on, a.clip);
-                        zst[pi] = F(pz);
-                        const float r = F(pr);
-                        store_coherent(snext + (size_t)rl * Hp + gu, r * hp);   // r (.) H_prev
-                    } else {                                // lbr = 0: candidate
-                        float ph_ = xv[2] + rec_at(rl, a.NTA * 16 + u);
-                        ph_ = ph_ + cst_u[2 * a.U + u];
-                        ph_ = ph_ + cst_u[6 * a.U + u];
-                        ph_ = clip_pre(ph_, a.clip_on, a.clip);
-                        const float ht = Gf(ph_);
-                        const float z = zst[pi];
-                        const float omz = 1.0f - z;
-                        const float a1 = omz * ht;
-                        const float a2 = z * hp;
-                        hn = a1 + a2;
-                    }
-                } else {                                    // LSTM: i, o, f, c
-                    float pre[4];
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        float v = xv[g] + rec_at(rl, g * uc + u);
-                        v = v + cst_u[g * a.U + u];
-                        v = v + cst_u[(4 + g) * a.U + u];
-                        pre[g] = v;
-                    }
-                    const float cp = cn;
-                    if (Pd) {
-                        const float pi_ = cst_u[8 * a.U + u] * cp;
-                        const float pf_ = cst_u[10 * a.U + u] * cp;
-                        pre[0] = pre[0] + pi_;
-                        pre[2] = pre[2] + pf_;
-                    }
-                    const float ci = clip_pre(pre[0], a.clip_on, a.clip);
-                    const float cf = clip_pre(pre[2], a.clip_on, a.clip);
-                    const float cc = clip_pre(pre[3], a.clip_on, a.clip);
-                    const float ig = F(ci);
-                    const float fg =
-                        a.input_forget ? 1.0f - ig : F(cf);
-                    const float ct = Gf(cc);
-                    const float k1 = fg * cp;
-                    const float k2 = ig * ct;
-                    cn = k1 + k2;
-                    float po = pre[1];
-                    if (Pd) {
-                        const float pov = cst_u[9 * a.U + u] * cn;
-                        po = po + pov;
-                    }
-                    po = clip_pre(po, a.clip_on, a.clip);
-                    const float og = F(po);
-                    const float hc = Hf(cn);
-                    hn = og * hc;
+                if (op != RNN_OP_GRU || a.phases == 1) {    // (compile-time for LSTM, RNN)
+                    hn = gates_one_phase(
+                        op, xv, [&](int g) { return rec_at(rl, g * uc + u); }, cst_u, a.U, u,
+                        Pd != nullptr, a.clip_on, a.clip, a.input_forget != 0, hp, cn, F, Gf, Hf);
+                } else if (ph == 0) {                       // GRU lbr = 0: z and r
+                    float pz = xv[0] + rec_at(rl, u);
+                    float pr = xv[1] + rec_at(rl, uc + u);
+                    pz = pz + cst_u[u];
+                    pz = pz + cst_u[4 * a.U + u];
+                    pr = pr + cst_u[a.U + u];
+                    pr = pr + cst_u[5 * a.U + u];
+                    pz = clip_pre(pz, a.clip_on, a.clip);
+                    pr = clip_pre(pr, a.clip_on, a.clip);
+                    zst[pi] = F(pz);
+                    const float r = F(pr);
+                    store_coherent(snext + (size_t)rl * Hp + gu, r * hp);   // r (.) H_prev
+                } else {                                    // GRU lbr = 0: candidate
+                    float ph_ = xv[2] + rec_at(rl, a.NTA * 16 + u);
+                    ph_ = ph_ + cst_u[2 * a.U + u];
+                    ph_ = ph_ + cst_u[6 * a.U + u];
+                    ph_ = clip_pre(ph_, a.clip_on, a.clip);
+                    const float ht = Gf(ph_);
+                    const float z = zst[pi];
+                    const float omz = 1.0f - z;
+                    const float a1 = omz * ht;
+                    const float a2 = z * hp;
+                    hn = a1 + a2;
                 }
             } else if (a.phases == 2 && ph == 0) {
                 store_coherent(snext + (size_t)rl * Hp + gu, 0.0f);
@@ -550,8 +568,8 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
                 store_coherent(pl + (size_t)(e / padw) * Hp + a.H + e % padw, 0.0f);
         }
         if (q + 1 < a.q_end)
-            group_barrier(a.bar + (size_t)grp * a.NUB, a.NUB, ub, (uint32_t)(q + 1), a.err,
-                          a.spin_limit, dead);
+            group_barrier(a.bar + (size_t)grp * 2 * a.NUB, a.NUB, ub, (uint32_t)(q + 1), a.err,
+                          a.spin_limit, a.withhold_flags != 0, dead);
         else
             __syncthreads();
     }

@@ -1,0 +1,436 @@
+// recurrence_pipe.h -- the step loop (same operator semantics as
+// recurrence_kernel.h: onemodel "Recurrent operators", section "Computation",
+// the pre-activation / LSTM / GRU / RNN paragraphs, "Choices the
+// specification leaves open" for masking and reverse traversal, "Exact mode"
+// for NaN canonicalisation) software-pipelined over two half-batch sub-steps.
+//
+// The workgroup's BT rows are processed as two halves of BT/2 rows, one after
+// the other, every step: product, reduction and gate arithmetic of half 0,
+// then of half 1.  Each half has flags of its own, so the exchange of one
+// half's new H (store completion, flag store, the other workgroups' polls)
+// proceeds while the workgroup computes the other half's product, instead of
+// stalling every wave between steps:
+//   - a half's flag is published from inside the NEXT product (the other
+//     half's), at a fixed k block: each wave waits there for its own H stores
+//     to complete and the last wave of the four to arrive stores the flag;
+//   - before a half's product, each wave waits only for the flags of the
+//     workgroups that produce its own k range of H.
+// The waves split k and sum their partial tiles exactly as the four-wave
+// kernel does (same fragments, same MFMA order per output, same wave order),
+// so the results are bit-identical to it.  Single-phase operators (RNN, LSTM,
+// GRU with linear_before_reset = 1) with R resident in registers.
+#pragma once
+
+#include "recurrence_kernel.h"
+
+namespace rnnamd {
+
+// Wait until flags[0 .. n) all reach `target` (one wave; every lane reads a
+// share of the flags).  More than spin_limit polls raises the error word and
+// stops waiting.
+__device__ __forceinline__ void wave_wait_flags(const uint32_t *flags, int n, uint32_t target,
+                                                int32_t *err, uint32_t spin_limit, bool &dead)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t polls = 0;
+    for (;;) {
+        bool ok = true;
+        for (int i = lane; i < n; i += 64)
+            ok = ok && __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target;
+        if (__all(ok))
+            break;
+        __builtin_amdgcn_s_sleep(1);
+        if (++polls > spin_limit) {
+            if (lane == 0)
+                __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            dead = true;
+            break;
+        }
+    }
+    asm volatile("" ::: "memory");   // no later load is moved above the wait
+}
+
+// The register-resident product (as product_res) with A tiles prefetched PD
+// k blocks ahead.  The first PD blocks are loaded by prime_ring beforehand
+// (so that their latency overlaps other work); `mid` runs right after the
+// last A prefetch, `hook` at the top of k block KH, before that block's
+// prefetch is issued, and `late` at the top of k block KP (after every A
+// prefetch when KP >= KBR - PD).
+template <int MT, int KBR, int PD>
+__device__ __forceinline__ void prime_ring(f4 (&ring)[(PD < KBR ? PD : KBR) + 1][MT],
+                                           const float *asrc, int Hp)
+{
+    constexpr int D_ = PD < KBR ? PD : KBR;
+#pragma unroll
+    for (int p = 0; p < D_; ++p)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            ring[p][mt] = *(const f4 *)(asrc + (size_t)mt * 16 * Hp + p * 16);
+}
+
+template <int MT, int NT, int KBR, int PD, int KH, int KP, typename Mid, typename Hook,
+          typename Late>
+__device__ __forceinline__ void product_res_hooked(f4 (&acc)[MT][NT],
+                                                   f4 (&ring)[(PD < KBR ? PD : KBR) + 1][MT],
+                                                   const float *asrc, int Hp,
+                                                   const f4 (&rr)[NT][KBR], Mid mid, Hook hook,
+                                                   Late late)
+{
+    constexpr int D_ = PD < KBR ? PD : KBR;
+    if constexpr (D_ >= KBR)
+        mid();
+#pragma unroll
+    for (int kb = 0; kb < KBR; ++kb) {
+        if (kb == KH)
+            hook();
+        if (kb == KP)
+            late();
+        if (kb + D_ < KBR) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                ring[(kb + D_) % (D_ + 1)][mt] =
+                    *(const f4 *)(asrc + (size_t)mt * 16 * Hp + (kb + D_) * 16);
+            if (kb + D_ == KBR - 1)
+                mid();
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                        ring[kb % (D_ + 1)][mt][s], rr[nt][kb][s], acc[mt][nt], 0, 0, 0);
+    }
+}
+
+// LDS bytes: partial tiles of both halves, h and c per pair, lengths, the
+// per-unit constants, two publish counters.
+__host__ __device__ inline size_t rec_pipe_lds_bytes(int bt, int nt, int u)
+{
+    return ((size_t)4 * bt * (nt * 16 + 4) + 2 * (size_t)bt * u + bt + 11 * (size_t)u + 2) * 4;
+}
+
+// Depth of the A prefetch for the half-height products (fewer MFMAs per k
+// block than the full tile, so more blocks in flight).
+constexpr int kPipePrefetch = 2;
+
+template <int MTH, int NT, int KBR, int ACT>
+__global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
+{
+    constexpr int BTH = MTH * 16;                // rows per half
+    constexpr int BT = 2 * BTH;
+    constexpr int NTC = NT * 16;
+    constexpr int LDR = NTC + 4;
+    constexpr int P = 2;                         // pairs per thread and half, at most
+    constexpr int KH = KBR / 2;                  // k block where the other half is published
+    constexpr int KP = KBR - (kPipePrefetch < KBR ? kPipePrefetch : KBR);   // ... where the next is polled
+    static_assert(KP > KH, "the poll follows the publish");
+    // Poll the next product's flags inside this product and load its first k
+    // blocks before this half's gate arithmetic only when the product is long
+    // enough (>= 128 MFMAs per wave) to hide the poll's memory round trip;
+    // short products wait for their flags right before they start.
+    constexpr bool EARLY = 4 * MTH * NT * KBR >= 128;
+    extern __shared__ float smem[];
+    float *red = smem;                           // [2 halves][4 waves][BTH][LDR] partial tiles
+    float *hst = red + 8 * BTH * LDR;            // [BT * U] h of each (row, unit) pair
+    float *cst = hst + BT * a.U;                 // [BT * U] LSTM cell state
+    int *lst = (int *)(cst + BT * a.U);          // [BT] sequence length of each row
+    float *cst_u = (float *)(lst + BT);          // [11][U] Wb, Rb per gate, then Pi, Po, Pf
+    uint32_t *ctr = (uint32_t *)(cst_u + 11 * a.U);   // [2] arrivals at each half's publish
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
+
+    // same workgroup -> (d, batch block, unit block) map as the four-wave kernel
+    const int nwg = gridDim.x;
+    const int wg = blockIdx.x;
+    const int lg = (nwg % 8 == 0) ? (wg % 8) * (nwg / 8) + wg / 8 : wg;
+    const int ub = lg % a.NUB;
+    const int bb = (lg / a.NUB) % a.NBB;
+    const int d = lg / (a.NUB * a.NBB);
+    const int u0 = ub * a.U;
+    const int uc = min(a.U, a.H - u0);
+    const int row0 = bb * BT;
+    const int rows = min(BT, a.Bt - row0);
+    const int Hp = a.Hp;
+    const bool rev = a.reverse_only || d == 1;
+    const int GH = a.G * a.H;
+    const int op = ACT == 1 ? (int)RNN_OP_LSTM
+                 : (ACT == 2 || ACT == 4) ? (int)RNN_OP_GRU
+                 : ACT == 3 ? (int)RNN_OP_RNN : a.op;
+    const size_t plane = (size_t)a.D * a.Btp * Hp;
+    const size_t drow = ((size_t)d * a.Btp + row0) * Hp;
+    const int grp = d * a.NBB + bb;
+    uint32_t *flags0 = a.bar + (size_t)grp * 2 * a.NUB;     // [2 halves][NUB]
+    const ActSpec fa = a.act[d][0], ga = a.act[d][1], ha = a.act[d][2];
+
+    const float *Wb = a.B ? a.B + (size_t)d * 2 * GH : nullptr;
+    const float *Rb = a.B ? Wb + GH : nullptr;
+    const float *Pd = a.P ? a.P + (size_t)d * 3 * a.H : nullptr;
+    const size_t xwd = (size_t)d * a.S * a.Bt * GH + (size_t)ub * a.G * a.U;
+    const int npairs = rows * uc;
+
+    // The unit blocks whose H columns this wave's k range reads (the columns
+    // [H, Hp) are written by the last unit block).
+    const int k0 = w * KBR * 16;
+    const int wub_lo = min(k0 / a.U, a.NUB - 1);
+    const int wub_hi = min(a.NUB - 1, (k0 + KBR * 16 - 1) / a.U);
+
+    // R fragments, as in the four-wave kernel
+    const float *rfrag = a.Rp + ((size_t)(d * a.NUB + ub) * NTC + lr) * Hp + k0 + 4 * lq;
+    f4 rr[NT][KBR];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int kb = 0; kb < KBR; ++kb)
+            rr[nt][kb] = *(const f4 *)(rfrag + (size_t)nt * 16 * Hp + kb * 16);
+
+    // states at the start of this launch, constants, counters
+    {
+        const int j0 = a.q_begin;
+        for (int pi = tid; pi < npairs; pi += 256) {
+            const int rl = pi / uc, u = pi - rl * uc;
+            hst[pi] = a.hbuf[(size_t)j0 * plane + drow + (size_t)rl * Hp + u0 + u];
+            cst[pi] = op == RNN_OP_LSTM ? a.cbuf[((size_t)d * a.Bt + row0 + rl) * a.H + u0 + u] : 0.0f;
+        }
+        for (int rl = tid; rl < rows; rl += 256)
+            lst[rl] = a.lens[row0 + rl];
+        // zeros when B is absent (adding +0 is the identity here: xw + rec is
+        // never -0, both sums starting at +0)
+        for (int e = tid; e < 11 * uc; e += 256) {
+            const int k = e / uc, u = e - k * uc;
+            float v = 0.0f;
+            if (k < 4 && k < a.G && Wb)
+                v = Wb[k * a.H + u0 + u];
+            else if (k >= 4 && k < 8 && k - 4 < a.G && Rb)
+                v = Rb[(k - 4) * a.H + u0 + u];
+            else if (k >= 8 && Pd)
+                v = Pd[(k - 8) * a.H + u0 + u];
+            cst_u[k * a.U + u] = v;
+        }
+        if (tid < 2)
+            ctr[tid] = 0u;
+        __syncthreads();
+    }
+
+    // this thread's pairs of half h: (local row, unit) = (h * BTH + i / uc,
+    // i % uc) for i = tid + 256 * k
+    auto hpairs_of = [&](int h) { return max(0, min(BTH, rows - h * BTH)) * uc; };
+    auto fetch_xw_q = [&](int qq, int h, int i, float *xv) {
+        xv[0] = xv[1] = xv[2] = xv[3] = 0.0f;
+        const int rl = h * BTH + i / uc, u = i % uc;
+        const int len = lst[rl];
+        if (qq >= len)
+            return;
+        const int t = rev ? len - 1 - qq : qq;
+        const float *src = a.XW + xwd + ((size_t)t * a.Bt + row0 + rl) * GH + u;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            if (g < a.G)
+                xv[g] = src[g * uc];
+    };
+    float xw_next[2][P][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            const int i = tid + 256 * k;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                xw_next[h][k][g] = 0.0f;
+            if (i < hpairs_of(h) && a.q_begin < a.q_end)
+                fetch_xw_q(a.q_begin, h, i, xw_next[h][k]);
+        }
+
+    bool dead = false;
+    // a publish left for the next product: half, flag value, generation
+    int pend_h = -1;
+    uint32_t pend_v = 0, pend_gen = 0;
+    uint32_t gens[2] = {0u, 0u};
+    auto publish = [&]() {
+        if (pend_h >= 0) {
+            wait_stores();                       // this wave's H stores have completed
+            if (lane == 0) {
+                const uint32_t old = __hip_atomic_fetch_add(ctr + pend_h, 1u, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (old == 4u * pend_gen + 3u && !a.withhold_flags)   // the last of the four waves
+                    __hip_atomic_store(flags0 + (size_t)pend_h * a.NUB + ub, pend_v,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            pend_h = -1;
+        }
+    };
+
+    // A operand of half h at step q: this wave's k range of its rows
+    auto a_src = [&](int qq, int h) {
+        return a.hbuf + (size_t)qq * plane + drow + (size_t)(h * BTH + lr) * Hp + k0 + 4 * lq;
+    };
+    constexpr int RING = (kPipePrefetch < KBR ? kPipePrefetch : KBR) + 1;
+    f4 ring[RING][MTH];
+    if (a.q_begin < a.q_end)
+        prime_ring<MTH, KBR, kPipePrefetch>(ring, a_src(a.q_begin, 0), Hp);
+    bool primed = true;                          // the next product's first blocks are loaded
+
+    for (int q = a.q_begin; q < a.q_end; ++q) {
+        const int j = q;                         // one phase per step
+        float *hnext = a.hbuf + (size_t)(j + 1) * plane + drow;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int hrow0 = h * BTH;
+            const int hpairs = hpairs_of(h);
+            // the next product: half 1 of this step, or half 0 of the next
+            const int nq = h == 0 ? q : q + 1, nh = 1 - h;
+            const bool has_next = nq < a.q_end;
+            if (!primed) {                       // its flags were not all set earlier
+                if (!dead)
+                    wave_wait_flags(flags0 + (size_t)h * a.NUB + wub_lo, wub_hi - wub_lo + 1,
+                                    (uint32_t)q, a.err, a.spin_limit, dead);
+                prime_ring<MTH, KBR, kPipePrefetch>(ring, a_src(q, h), Hp);
+            }
+            float xw[P][4];
+#pragma unroll
+            for (int k = 0; k < P; ++k)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    xw[k][g] = xw_next[h][k][g];
+            auto prefetch_xw = [&]() {
+                if (q + 1 < a.q_end) {
+#pragma unroll
+                    for (int k = 0; k < P; ++k) {
+                        const int i = tid + 256 * k;
+                        if (i < hpairs)
+                            fetch_xw_q(q + 1, h, i, xw_next[h][k]);
+                    }
+                }
+            };
+
+            // ---- product over this wave's k range, this half's rows ---------
+            // (its first k blocks were loaded by prime_ring)
+            f4 acc[MTH][NT];
+#pragma unroll
+            for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    acc[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
+            // The next product's flags (a step after the launch's first) are
+            // read once near the end of this product, after its last A
+            // prefetch, so that the loads return during its last MFMAs (one
+            // flag per lane; more than 64 flags: always wait later).
+            const uint32_t *nflags = flags0 + (size_t)nh * a.NUB + wub_lo;
+            const int nfl = wub_hi - wub_lo + 1;
+            const bool need_wait = has_next && nq > a.q_begin && !dead;
+            uint32_t fv = 0xffffffffu;
+            auto poll_next = [&]() {
+                if (EARLY && need_wait && nfl <= 64 && lane < nfl)
+                    fv = __hip_atomic_load(nflags + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            };
+            product_res_hooked<MTH, NT, KBR, kPipePrefetch, KH, KP>(
+                acc, ring, a_src(q, h), Hp, rr, prefetch_xw, publish, poll_next);
+            float *redh = red + h * 4 * BTH * LDR;
+#pragma unroll
+            for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        redh[(w * BTH + mt * 16 + 4 * lq + r) * LDR + nt * 16 + lr] = acc[mt][nt][r];
+            __syncthreads();
+            // if they were all set, load the next product's first k blocks now,
+            // so that their latency overlaps this half's gate arithmetic;
+            // otherwise wait for them only before that product
+            primed = !need_wait || (EARLY && nfl <= 64 && __all(fv >= (uint32_t)nq));
+            asm volatile("" ::: "memory");
+            if (has_next && primed)
+                prime_ring<MTH, KBR, kPipePrefetch>(ring, a_src(nq, nh), Hp);
+
+            // ---- gate arithmetic of this thread's pairs of half h -------------
+            auto run_pairs = [&](auto F, auto Gf, auto Hf) {
+#pragma unroll
+                for (int k = 0; k < P; ++k) {
+                    const int i = tid + 256 * k;
+                    if (i >= hpairs)
+                        continue;
+                    const int rh = i / uc, u = i - rh * uc;
+                    const int rl = hrow0 + rh;
+                    const int pi = rl * uc + u;
+                    const int b = row0 + rl;
+                    const int gu = u0 + u;
+                    const int len = lst[rl];
+                    const bool active = j < len;
+                    const float hp = hst[pi];
+                    float hn = hp, cn = cst[pi];
+                    if (active) {
+                        const float *rp = redh + rh * LDR + u;
+                        hn = gates_one_phase(
+                            op, xw[k],
+                            [&](int g) {
+                                const float *p = rp + g * uc;
+                                float v = p[0];
+#pragma unroll
+                                for (int w2 = 1; w2 < 4; ++w2)
+                                    v = v + p[w2 * BTH * LDR];   // fixed wave order
+                                return v;
+                            },
+                            cst_u, a.U, u, Pd != nullptr, a.clip_on, a.clip, a.input_forget != 0,
+                            hp, cn, F, Gf, Hf);
+                    }
+                    store_coherent(hnext + (size_t)rl * Hp + gu, hn);   // carried when inactive
+                    hst[pi] = hn;
+                    cst[pi] = cn;
+                    if (a.Y) {
+                        const int t = active ? (rev ? len - 1 - j : j) : j;
+                        const size_t yo = a.layout == 0
+                                              ? (((size_t)t * a.D + d) * a.Bt + b) * a.H + gu
+                                              : (((size_t)b * a.S + t) * a.D + d) * a.H + gu;
+                        a.Y[yo] = active ? canon_nan(hn) : 0.0f;
+                    }
+                }
+            };
+            if constexpr (ACT == 1 || ACT == 4)
+                run_pairs(ActSigmoid{}, ActTanh{}, ActTanh{});
+            else if constexpr (ACT == 2)
+                run_pairs(ActHardSigmoid{fa.alpha, fa.beta}, ActTanh{}, ActTanh{});
+            else if constexpr (ACT == 3)
+                run_pairs(ActTanh{}, ActTanh{}, ActTanh{});
+            else
+                run_pairs(ActAny{fa}, ActAny{ga}, ActAny{ha});
+            // the last unit block also zeroes this half's padding columns [H, Hp)
+            if (u0 + uc == a.H && Hp > a.H) {
+                const int padw = Hp - a.H;
+                const int hr = hpairs / uc;
+                for (int e = tid; e < hr * padw; e += 256)
+                    store_coherent(hnext + (size_t)(hrow0 + e / padw) * Hp + a.H + e % padw, 0.0f);
+            }
+            // published from inside the next product (there is one whenever a
+            // later step exists: half 1 of this step, or half 0 of the next)
+            if (q + 1 < a.q_end) {
+                pend_h = h;
+                pend_v = (uint32_t)(q + 1);
+                pend_gen = gens[h]++;
+            }
+        }
+    }
+
+    // ---- end of this launch: keep or publish the states ----------------------
+    __syncthreads();                             // (pairs were owned per half above)
+    const bool done = a.q_end == a.S;
+    for (int pi = tid; pi < npairs; pi += 256) {
+        const int rl = pi / uc, u = pi - rl * uc;
+        const int b = row0 + rl;
+        const size_t so = ((size_t)d * a.Bt + b) * a.H + u0 + u;
+        if (op == RNN_OP_LSTM)
+            a.cbuf[so] = cst[pi];
+        if (done) {
+            const size_t yo = a.layout == 0 ? so : ((size_t)b * a.D + d) * a.H + u0 + u;
+            const bool none = lst[rl] == 0;
+            if (a.Yh)
+                a.Yh[yo] = none ? 0.0f : canon_nan(hst[pi]);
+            if (a.Yc)
+                a.Yc[yo] = none ? 0.0f : canon_nan(cst[pi]);
+        }
+    }
+}
+
+}  // namespace rnnamd

@@ -64,6 +64,7 @@ RecArgs rec_args(const rnn_plan &p, unsigned char *ws, const float *B, const flo
     r.NT = p.NT;
     r.phases = p.phases;
     r.Btp = (int32_t)p.Btp;
+    r.halves = p.halves;
     r.reverse_only = p.reverse_only;
     r.layout = p.layout;
     r.clip_on = p.clip_on;
@@ -84,8 +85,9 @@ RecArgs rec_args(const rnn_plan &p, unsigned char *ws, const float *B, const flo
     r.Yh = Yh;
     r.Yc = Yc;
     r.bar = (uint32_t *)(ws + p.ws.bar);
-    r.err = (int32_t *)(ws + p.ws.bar) + p.D * p.NBB * p.NUB;
+    r.err = (int32_t *)(ws + p.ws.bar) + n_flags(p);
     r.spin_limit = p.spin_limit;
+    r.withhold_flags = p.withhold_flags;
     r.q_begin = 0;
     r.q_end = (int32_t)(p.S * p.phases);
     return r;
@@ -235,7 +237,7 @@ extern "C" rnn_status rnn_run(rnn_plan *p, void *hip_stream, void *workspace, si
     ia.lens_dev = lens_dev;
     ia.fill_lens = sequence_lens ? -1 : (int32_t)p->S;
     ia.bar = (uint32_t *)(ws + p->ws.bar);
-    ia.n_bar = p->D * p->NBB * p->NUB;
+    ia.n_bar = n_flags(*p);
     ia.D = p->D;
     ia.Bt = p->Bt;
     ia.Btp = p->Btp;
@@ -300,7 +302,7 @@ extern "C" rnn_status rnn_workspace_check(const rnn_plan *p, void *hip_stream, c
         return hip_fail(e, "hipStreamSynchronize");
     int32_t err = 0;
     const unsigned char *ws = (const unsigned char *)workspace;
-    e = hipMemcpy(&err, ws + p->ws.bar + (size_t)p->D * p->NBB * p->NUB * 4, 4, hipMemcpyDeviceToHost);
+    e = hipMemcpy(&err, ws + p->ws.bar + (size_t)n_flags(*p) * 4, 4, hipMemcpyDeviceToHost);
     if (e != hipSuccess)
         return hip_fail(e, "error word read");
     if (err) {

@@ -349,24 +349,71 @@ def test_resident_kernels_without_bias_match_oracle(op, attrs):
     compare(c, run_gpu(c))
 
 
-def test_a_stalled_barrier_raises_the_device_error_and_the_kernel_exits():
-    # A spin limit of 1 lets each step barrier poll twice before it gives up:
-    # with 256 co-resident workgroups their arrival skew alone exceeds that,
-    # so a barrier times out; the kernel then runs on without waiting and
-    # exits normally, and rnn_workspace_check reports the error it raised.
+@pytest.mark.parametrize("halves", [1, 2])
+def test_a_stalled_barrier_raises_the_device_error_and_the_kernel_exits(halves, monkeypatch):
+    # Forced from the host: with RNN_AMD_TEST_WITHHOLD_FLAGS the step loops
+    # never store their flags, so every wait between steps runs out its spin
+    # limit (1: two polls); the kernel then runs on without waiting and exits
+    # normally, and rnn_workspace_check reports the error it raised.
     c = workloads.random_case("LSTM", "bidirectional", 8, 64, 16, 1024, seed=3, with_h0=True,
                               scale=1.0 / 32)
-    say(f"case {c.name} with barrier_spin_limit=1")
-    plan = ra.plan_for_case(c, kernel_path=ra.RNN_PATH_PERSISTENT, barrier_spin_limit=1)
-    assert "workgroups=256" in plan.describe()
+    say(f"case {c.name} with withheld flags, barrier_spin_limit=1, batch_halves={halves}")
+    monkeypatch.setenv("RNN_AMD_TEST_WITHHOLD_FLAGS", "1")
+    plan = ra.plan_for_case(c, kernel_path=ra.RNN_PATH_PERSISTENT, barrier_spin_limit=1,
+                            batch_halves=halves)
+    monkeypatch.delenv("RNN_AMD_TEST_WITHHOLD_FLAGS")
+    assert "workgroups=256" in plan.describe() and f"halves={halves}" in plan.describe()
     ra.run_case(c, plan=plan)
     torch.cuda.synchronize()
     with pytest.raises(ra.RNNError) as ei:
         plan.check()
     assert ei.value.status == ra.RNN_ERR_DEVICE
-    # the default limit on the same inputs is clean and matches the oracle
-    plan2 = ra.plan_for_case(c, kernel_path=ra.RNN_PATH_PERSISTENT)
+    # a plan made without the switch, on the same inputs, is clean and matches the oracle
+    plan2 = ra.plan_for_case(c, kernel_path=ra.RNN_PATH_PERSISTENT, batch_halves=halves)
     out = ra.run_case(c, plan=plan2)
     torch.cuda.synchronize()
     plan2.check()
     compare(c, [to_np(x) for x in out])
+
+
+# ---------------------------------------------------------------------------
+# Two half-batch groups of waves: bit-identical to one group, and to the oracle
+# ---------------------------------------------------------------------------
+
+HALVES = [
+    # 2 tiles per half, 2 column tiles, 16 k blocks per wave; peepholes, clip
+    dict(op="LSTM", direction="bidirectional", S=7, Bt=64, I=40, H=1024, with_p=True, clip=0.9,
+         with_lens=True),
+    # ragged second half (18 of 32 rows), padded hidden (500 -> 512), layout 1
+    dict(op="GRU", direction="reverse", S=6, Bt=50, I=24, H=500, linear_before_reset=1,
+         layout=1, with_lens=True),
+    # one tile per half (batch tile 32), second half 4 rows
+    dict(op="RNN", direction="forward", S=9, Bt=20, I=16, H=512, with_lens=True),
+    # HardSigmoid GRU (its own compiled set), half 1 with 8 rows
+    dict(op="GRU", direction="bidirectional", S=5, Bt=40, I=12, H=512, linear_before_reset=1,
+         activations=["HardSigmoid", "Tanh"], alpha=[0.25], beta=[0.45]),
+    # a set compiled through the run-time switch, input_forget
+    dict(op="LSTM", direction="forward", S=5, Bt=33, I=10, H=480, input_forget=1,
+         activations=["HardSigmoid", "Softsign", "Tanh"], alpha=[0.3], beta=[0.5]),
+]
+
+
+@pytest.mark.parametrize("k", range(len(HALVES)))
+def test_half_batch_halves_match_one_group_bitwise_and_the_oracle(k):
+    spec = dict(HALVES[k])
+    op, direction = spec.pop("op"), spec.pop("direction")
+    S, Bt, I, H = spec.pop("S"), spec.pop("Bt"), spec.pop("I"), spec.pop("H")
+    lay = spec.pop("layout", 0)
+    kw = {key: spec.pop(key) for key in ("with_lens", "with_p") if key in spec}
+    c = workloads.random_case(op, direction, S, Bt, I, H, seed=700 + k, layout=lay,
+                              with_h0=True, with_c0=(op == "LSTM"), scale=1.5 / H ** 0.5,
+                              **kw, **spec)
+    say(f"case {c.name} {HALVES[k]}")
+    assert "halves=2" in ra.plan_for_case(c).describe()
+    two = run_gpu(c, batch_halves=2)
+    one = run_gpu(c, batch_halves=1)
+    assert _digest(two) == _digest(one)
+    compare(c, two)
+    if k == 0:
+        per_step = run_gpu(c, batch_halves=2, kernel_path=ra.RNN_PATH_PER_STEP)
+        assert _digest(per_step) == _digest(two)
