@@ -17,13 +17,16 @@ namespace rnnamd {
 
 // Fast-mode forms of the two default activations ("Fast mode": elementwise
 // functions use fast approximations).  exp is the hardware base-2 exponential
-// of x*log2(e) and 1/y the hardware reciprocal; absolute error below 3e-7 on
-// all of R.  NaN gives NaN; +-inf give the limits.
+// of x*log2(e) and 1/y the hardware reciprocal (v_rcp_f32, within 1 ulp; its
+// argument here is >= 1, never subnormal); absolute error below 3e-7 on all
+// of R.  NaN gives NaN; +-inf give the limits.
+__device__ __forceinline__ float fast_rcp(float y) { return __builtin_amdgcn_rcpf(y); }
+
 __device__ __forceinline__ float fast_sigmoid(float x)
 {
     const float e = __expf(-x);          // inf for x << 0, 0 for x >> 0
     const float den = 1.0f + e;
-    return __frcp_rn(den);
+    return fast_rcp(den);
 }
 
 __device__ __forceinline__ float fast_tanh(float x)
@@ -32,7 +35,7 @@ __device__ __forceinline__ float fast_tanh(float x)
     const float ax = fabsf(x);
     const float e = __expf(2.0f * ax);
     const float den = e + 1.0f;
-    const float q = 2.0f * __frcp_rn(den);
+    const float q = 2.0f * fast_rcp(den);
     const float t = 1.0f - q;
     return copysignf(t, x);
 }

@@ -216,11 +216,20 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
     }
 
     // this thread's pairs of half h: (local row, unit) = (h * BTH + i / uc,
-    // i % uc) for i = tid + 256 * k
+    // i % uc) for i = tid + 256 * k, decoded once as (row << 16) | unit, or
+    // -1 where the half has fewer pairs
     auto hpairs_of = [&](int h) { return max(0, min(BTH, rows - h * BTH)) * uc; };
-    auto fetch_xw_q = [&](int qq, int h, int i, float *xv) {
+    int pk[2][P];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            const int i = tid + 256 * k;
+            pk[h][k] = i < hpairs_of(h) ? ((h * BTH + i / uc) << 16) | (i % uc) : -1;
+        }
+    auto fetch_xw_q = [&](int qq, int h, int k, float *xv) {
         xv[0] = xv[1] = xv[2] = xv[3] = 0.0f;
-        const int rl = h * BTH + i / uc, u = i % uc;
+        const int rl = pk[h][k] >> 16, u = pk[h][k] & 0xffff;
         const int len = lst[rl];
         if (qq >= len)
             return;
@@ -236,12 +245,11 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
     for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int k = 0; k < P; ++k) {
-            const int i = tid + 256 * k;
 #pragma unroll
             for (int g = 0; g < 4; ++g)
                 xw_next[h][k][g] = 0.0f;
-            if (i < hpairs_of(h) && a.q_begin < a.q_end)
-                fetch_xw_q(a.q_begin, h, i, xw_next[h][k]);
+            if (pk[h][k] >= 0 && a.q_begin < a.q_end)
+                fetch_xw_q(a.q_begin, h, k, xw_next[h][k]);
         }
 
     bool dead = false;
@@ -298,11 +306,9 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
             auto prefetch_xw = [&]() {
                 if (q + 1 < a.q_end) {
 #pragma unroll
-                    for (int k = 0; k < P; ++k) {
-                        const int i = tid + 256 * k;
-                        if (i < hpairs)
-                            fetch_xw_q(q + 1, h, i, xw_next[h][k]);
-                    }
+                    for (int k = 0; k < P; ++k)
+                        if (pk[h][k] >= 0)
+                            fetch_xw_q(q + 1, h, k, xw_next[h][k]);
                 }
             };
 
@@ -349,11 +355,10 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
             auto run_pairs = [&](auto F, auto Gf, auto Hf) {
 #pragma unroll
                 for (int k = 0; k < P; ++k) {
-                    const int i = tid + 256 * k;
-                    if (i >= hpairs)
+                    if (pk[h][k] < 0)
                         continue;
-                    const int rh = i / uc, u = i - rh * uc;
-                    const int rl = hrow0 + rh;
+                    const int rl = pk[h][k] >> 16, u = pk[h][k] & 0xffff;
+                    const int rh = rl - hrow0;
                     const int pi = rl * uc + u;
                     const int b = row0 + rl;
                     const int gu = u0 + u;
