@@ -45,6 +45,9 @@ def parse():
                                                           "COPY_WRITE_DIR"),
                    help="summarise four rocprofv3 --pmc csv runs (FETCH_SIZE / WRITE_SIZE of the "
                         "bench and of --copy-calibration) into per-launch HBM bytes, as JSON")
+    p.add_argument("--counter-summary", metavar="PMC_DIR",
+                   help="mean of every counter per dispatch of each kernel in a rocprofv3 --pmc "
+                        "csv run, as JSON")
     return p.parse_args()
 
 
@@ -83,19 +86,34 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES}), flush=True)
 
 
-def _pmc_rows(d):
-    """(kernel name, dispatch id, counter value) from every rocprofv3 counter
-    csv below directory d."""
+def _pmc_rows(d, counter=False):
+    """(kernel name, dispatch id, [counter name,] counter value) from every
+    rocprofv3 counter csv below directory d."""
     import csv
     import glob
     rows = []
     for fn in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
         with open(fn, newline="") as f:
             for r in csv.DictReader(f):
-                rows.append((r["Kernel_Name"], int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+                v = float(r["Counter_Value"])
+                rows.append((r["Kernel_Name"], int(r["Dispatch_Id"]), r["Counter_Name"], v) if counter
+                            else (r["Kernel_Name"], int(r["Dispatch_Id"]), v))
     if not rows:
         raise SystemExit(f"no counter_collection.csv under {d}")
     return rows
+
+
+def counter_summary(d):
+    """Mean over dispatches of each counter, per kernel (counters of one
+    dispatch with several rows, e.g. per dimension, are summed first)."""
+    import numpy as np
+    acc = {}
+    for name, did, ctr, v in _pmc_rows(d, counter=True):
+        k = acc.setdefault(name, {}).setdefault(ctr, {})
+        k[did] = k.get(did, 0.0) + v
+    out = {n: {c: {"mean": float(np.mean(list(v.values()))), "dispatches": len(v)}
+               for c, v in cs.items()} for n, cs in acc.items()}
+    print(json.dumps(out, indent=1))
 
 
 def traffic_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, workload):
@@ -187,6 +205,9 @@ def main():
     args = parse()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary, workload=args.workload)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))

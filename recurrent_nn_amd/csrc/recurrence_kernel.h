@@ -118,13 +118,15 @@ __device__ __forceinline__ void product_res(f4 (&acc)[MT][NT], const float *asrc
                 mid();
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 4; ++s) {
 #pragma unroll
             for (int nt = T0; nt < T1; ++nt)
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
                     acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
                         ring[kb % (D_ + 1)][mt][s], rr[nt][kb][s], acc[mt][nt], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);   // keep the independent accumulators together
+        }
     }
 }
 
@@ -155,13 +157,15 @@ __device__ __forceinline__ void product_stream(f4 (&acc)[MT][NT], const float *a
                 mid();
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 4; ++s) {
 #pragma unroll
             for (int nt = T0; nt < T1; ++nt)
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
                     acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt][s], bv[nt][s],
                                                                        acc[mt][nt], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);   // keep the independent accumulators together
+        }
         if (kb + 1 < KB) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)

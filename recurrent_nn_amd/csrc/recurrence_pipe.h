@@ -94,13 +94,18 @@ __device__ __forceinline__ void product_res_hooked(f4 (&acc)[MT][NT],
                 mid();
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 4; ++s) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
                     acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
                         ring[kb % (D_ + 1)][mt][s], rr[nt][kb][s], acc[mt][nt], 0, 0, 0);
+            // keep the MT x NT independent accumulators of one k sub-block
+            // together: left alone, the scheduler groups them by row tile,
+            // leaving two dependent chains that stall the matrix pipe
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 }
 
@@ -112,8 +117,8 @@ __host__ __device__ inline size_t rec_pipe_lds_bytes(int bt, int nt, int u)
 }
 
 // Depth of the A prefetch for the half-height products (fewer MFMAs per k
-// block than the full tile, so more blocks in flight).
-constexpr int kPipePrefetch = 2;
+// block than the full tile, so more blocks in flight; 3 measured best).
+constexpr int kPipePrefetch = 3;
 
 template <int MTH, int NT, int KBR, int ACT>
 __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
@@ -124,8 +129,11 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
     constexpr int LDR = NTC + 4;
     constexpr int P = 2;                         // pairs per thread and half, at most
     constexpr int KH = KBR / 2;                  // k block where the other half is published
-    constexpr int KP = KBR - (kPipePrefetch < KBR ? kPipePrefetch : KBR);   // ... where the next is polled
-    static_assert(KP > KH, "the poll follows the publish");
+    // k block where the next product's flags are polled: after the publish
+    // and after the last A prefetch is issued
+    constexpr int KPF = KBR - (kPipePrefetch < KBR ? kPipePrefetch : KBR);
+    constexpr int KP = KPF > KH ? KPF : KH + 1;
+    static_assert(KP < KBR, "the poll falls inside the product");
     // Poll the next product's flags inside this product and load its first k
     // blocks before this half's gate arithmetic only when the product is long
     // enough (>= 128 MFMAs per wave) to hide the poll's memory round trip;
