@@ -129,7 +129,7 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs a)
     // staging: thread -> (row = tid / 8 + 32 i, chunk = tid % 8 of 16 bytes)
     const int srow = tid >> 3, sch = tid & 7;
     u4 ra[4], rb[4];
-    auto gload = [&](int64_t kt) {
+    auto gload = [&](int64_t kt, u4 (&ra)[4], u4 (&rb)[4]) {
         const int64_t kbase = kt * KS;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -150,7 +150,7 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs a)
             }
         }
     };
-    auto sstore = [&](int buf) {
+    auto sstore = [&](int buf, const u4 (&ra)[4], const u4 (&rb)[4]) {
         unsigned char *A = lds + buf * 2 * TILEB;
         unsigned char *B = A + TILEB;
 #pragma unroll
@@ -168,13 +168,7 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs a)
         for (int j = 0; j < 4; ++j)
             acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int buf = (int)(kt & 1);
-        if (kt + 1 < nk)
-            gload(kt + 1);
+    auto stage = [&](int buf) {
         const unsigned char *A = lds + buf * 2 * TILEB;
         const unsigned char *B = A + TILEB;
 #pragma unroll
@@ -203,12 +197,31 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs a)
                     }
                 }
         }
+    };
+    gload(0, ra, rb);
+    sstore(0, ra, rb);
+    __syncthreads();
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int buf = (int)(kt & 1);
         if (kt + 1 < nk)
-            sstore(buf ^ 1);
+            gload(kt + 1, ra, rb);
+        stage(buf);
+        if (kt + 1 < nk)
+            sstore(buf ^ 1, ra, rb);
         __syncthreads();
     }
 
-    // store: lane holds rows 4*lq + r, column lr of each 16x16 tile
+    // store: lane holds rows 4*lq + r, column lr of each 16x16 tile.  The
+    // direction of a column and the row permutation of layout 1 are resolved
+    // once per column / row (32-bit divisions: M, N < 2^31 here).
+    size_t colbase[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + wn * 64 + j * 16 + lr;
+        const uint32_t d = n < a.N ? (uint32_t)n / (uint32_t)a.GH : 0u;
+        colbase[j] = n < a.N ? (size_t)d * a.S * a.Bt * a.GH + (size_t)(n - (int64_t)d * a.GH)
+                             : ~(size_t)0;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -216,21 +229,18 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs a)
             const int64_t m = m0 + wm * 64 + i * 16 + lq * 4 + r;
             if (m >= a.M)
                 continue;
-            int64_t xrow;   // row of XW[d] = t * Bt + b
+            size_t xrow;    // row of XW[d] = t * Bt + b
             if (a.layout == 0) {
-                xrow = m;
+                xrow = (size_t)m;
             } else {
-                const int64_t b = m / a.S, t = m - b * a.S;
-                xrow = t * a.Bt + b;
+                const uint32_t b = (uint32_t)m / (uint32_t)a.S, t = (uint32_t)m - b * (uint32_t)a.S;
+                xrow = (size_t)t * a.Bt + b;
             }
+            const size_t ro = xrow * a.GH;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t n = n0 + wn * 64 + j * 16 + lr;
-                if (n >= a.N)
-                    continue;
-                const int64_t d = n / a.GH, nl = n - d * a.GH;
-                a.XW[(d * a.S * a.Bt + xrow) * a.GH + nl] = acc[i][j][r];
-            }
+            for (int j = 0; j < 4; ++j)
+                if (colbase[j] != ~(size_t)0)
+                    a.XW[colbase[j] + ro] = acc[i][j][r];
         }
 }
 
