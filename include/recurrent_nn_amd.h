@@ -165,6 +165,35 @@ rnn_status rnn_run(rnn_plan *plan, void *hip_stream, void *workspace, size_t wor
                    float *Y, float *Y_h, float *Y_c);
 
 /*
+ * rnn_cell_run -- one step of the operator in the single-cell convention of
+ * the OpenVINO page "RNNCell-3" (sections "Inputs" and "Outputs"; its formula
+ * Ht = f(Xt Wi^T + Ht-1 Ri^T + Wbi + Rbi) in the description): the same
+ * operator as rnn_run at seq_length 1, except that the bias is ONE vector,
+ * the sum of the W and R biases, and only the new state is produced.
+ *   plan: created with dims.seq_length = 1 and dims.num_directions = 1 (any
+ *   op; the cell page itself defines the RNN cell, and the same convention is
+ *   applied to GRU and LSTM gates).
+ *   X [batch, input]; H [batch, hidden] (NULL = zeros); C [batch, hidden]
+ *   (LSTM only, NULL = zeros); W [G*hidden, input]; R [G*hidden, hidden];
+ *   B_sum [G*hidden] summed biases in the operator's gate order (NULL = no
+ *   bias); P [3*hidden] (LSTM peepholes, NULL = none) -- all DEVICE pointers.
+ *   H_out [batch, hidden] (required), C_out [batch, hidden] (LSTM only,
+ *   nullable): the state after the step.  NaN is written as 0x7FC00000.
+ *   The summed bias enters as ((X Wi^T + H Ri^T) + B_sum); internally it is
+ *   the ONNX B with Wb = B_sum and Rb = +0, which is exact.  It is staged in
+ *   the workspace, so the same workspace rules as rnn_run apply.
+ *   Errors (nothing is enqueued): those of rnn_run, plus InvalidInput when
+ *   the plan is not single-step and single-direction, when H_out is NULL, or
+ *   when B_sum is given for GRU with linear_before_reset = 1 (its recurrent
+ *   candidate bias is multiplied by the reset gate, so a sum cannot carry it:
+ *   use rnn_run with the full B there).
+ */
+rnn_status rnn_cell_run(rnn_plan *plan, void *hip_stream, void *workspace, size_t workspace_bytes,
+                        const float *X, const float *H, const float *C, const float *W,
+                        const float *R, const float *B_sum, const float *P, float *H_out,
+                        float *C_out);
+
+/*
  * rnn_workspace_check -- wait for `hip_stream`, then read the device-side
  * error word that the last run on this workspace left (a step barrier that
  * timed out).  RNN_OK when clean, RNN_ERR_DEVICE otherwise.  For tests of

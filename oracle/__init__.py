@@ -162,6 +162,38 @@ def run(case, n_threads: Optional[int] = None, want_y: bool = True,
     return st, Y, Yh, Yc
 
 
+def run_cell(op: str, X, W, R, B_sum=None, H=None, C=None, P=None,
+             activations: Optional[Sequence[str]] = None,
+             alpha: Optional[Sequence[float]] = None, beta: Optional[Sequence[float]] = None,
+             clip: Optional[float] = None, input_forget: int = 0, linear_before_reset: int = 0,
+             n_threads: Optional[int] = None):
+    """One step in the single-cell convention of the OpenVINO page "RNNCell-3"
+    ("Inputs": X [batch, input], H [batch, hidden], W, R, and B the SUM of the
+    W and R biases; "Outputs": the new hidden state only).  Reading: the summed
+    bias is the ONNX B with Wb = B and Rb = 0 (so the pre-activation is
+    (X Wi^T + H Ri^T) + B), applied to the gates of any operator; for GRU with
+    linear_before_reset = 1 the recurrent candidate bias is scaled by the reset
+    gate, so a sum cannot carry it and B_sum is refused.
+    Returns (H_out [batch, hidden], C_out [batch, hidden] or None)."""
+    from types import SimpleNamespace
+    X, W, R = _np32(X), _np32(W), _np32(R)
+    Bs, H0, C0, P0 = _np32(B_sum), _np32(H), _np32(C), _np32(P)
+    if Bs is not None and op == "GRU" and linear_before_reset:
+        raise ValueError("a summed bias cannot express GRU with linear_before_reset = 1")
+    Bt, I = X.shape
+    Hd = R.shape[1]
+    B = None if Bs is None else np.concatenate([Bs, np.zeros_like(Bs)])[None]
+    case = SimpleNamespace(
+        op=op, direction="forward", seq=1, batch=Bt, input=I, hidden=Hd, layout=0,
+        activations=activations, alpha=alpha, beta=beta, clip=clip, input_forget=input_forget,
+        linear_before_reset=linear_before_reset, proj_bf16=False, hidden_size_attr=0,
+        X=X[None], W=W[None], R=R[None], B=B, P=None if P0 is None else P0[None],
+        initial_h=None if H0 is None else H0[None],
+        initial_c=None if C0 is None else C0[None], sequence_lens=None)
+    _, _, Yh, Yc = run(case, n_threads=n_threads, want_y=False)
+    return Yh[0], (Yc[0] if Yc is not None else None)
+
+
 def activation(name: str, x, alpha: float = 0.0, beta: float = 0.0) -> np.ndarray:
     """One activation over an array, through the oracle's scalar function."""
     L = lib()

@@ -68,6 +68,13 @@ def rnn_run(plan: int, stream: int, workspace: int, workspace_bytes: int, X: int
                                initial_h, initial_c, P, Y, Y_h, Y_c)
 
 
+def rnn_cell_run(plan: int, stream: int, workspace: int, workspace_bytes: int, X: int, H: int,
+                 C: int, W: int, R: int, B_sum: int, P: int, H_out: int, C_out: int) -> int:
+    """Device pointers as ints (0 = NULL)."""
+    return _lib.load().rnn_cell_run(plan, stream, workspace, workspace_bytes, X, H, C, W, R, B_sum,
+                                    P, H_out, C_out)
+
+
 def rnn_workspace_check(plan: int, stream: int, workspace: int) -> int:
     return _lib.load().rnn_workspace_check(plan, stream, workspace)
 
@@ -240,6 +247,40 @@ class RNNPlan:
                      self._ptr(Y), self._ptr(Yh), self._ptr(Yc))
         _check(st, "rnn_run")
         return Y, Yh, Yc
+
+
+class RNNCell(RNNPlan):
+    """One step in the single-cell convention (rnn_cell_run): summed bias,
+    new state only.  ``op`` "RNN", "GRU" or "LSTM"; attributes as RNNPlan."""
+
+    def __init__(self, op: str, batch: int, input_size: int, hidden: int, **attrs):
+        super().__init__(op, 1, batch, input_size, hidden, num_directions=1, direction="forward",
+                         **attrs)
+
+    def step(self, X, W, R, B_sum=None, H=None, C=None, P=None, out=None, stream=None):
+        """X [batch, input], W [G*hidden, input], R [G*hidden, hidden],
+        B_sum [G*hidden], H / C [batch, hidden] (torch device tensors);
+        returns (H_out, C_out or None)."""
+        import torch
+        for name, t in (("X", X), ("W", W), ("R", R), ("B_sum", B_sum), ("H", H), ("C", C),
+                        ("P", P)):
+            if t is not None:
+                if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+                    raise ValueError(f"{name} must be a contiguous float32 device tensor")
+        dev = X.device
+        Bt, Hd = self.dims.batch_size, self.dims.hidden
+        if out is not None:
+            Ho, Co = out
+        else:
+            Ho = torch.empty((Bt, Hd), dtype=torch.float32, device=dev)
+            Co = torch.empty((Bt, Hd), dtype=torch.float32, device=dev) if self.op == "LSTM" else None
+        ws = self.workspace(dev)
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        p = self._ptr
+        st = rnn_cell_run(self.plan, s.cuda_stream, p(ws), self.workspace_bytes, p(X), p(H), p(C),
+                          p(W), p(R), p(B_sum), p(P), p(Ho), p(Co))
+        _check(st, "rnn_cell_run")
+        return Ho, Co
 
 
 def plan_for_case(case, **extra) -> RNNPlan:

@@ -20,7 +20,8 @@ RNN_PATH_AUTO, RNN_PATH_PERSISTENT, RNN_PATH_PER_STEP = 0, 1, 2
 STATUS_NAMES = {0: "RNN_OK", 1: "RNN_ERR_INVALID_INPUT", 2: "RNN_ERR_UNSUPPORTED",
                 3: "RNN_ERR_DEVICE", 4: "RNN_ERR_OUT_OF_MEMORY"}
 
-EXPORTED = ["rnn_plan_create", "rnn_plan_workspace_size", "rnn_run", "rnn_workspace_check",
+EXPORTED = ["rnn_plan_create", "rnn_plan_workspace_size", "rnn_run", "rnn_cell_run",
+            "rnn_workspace_check",
             "rnn_plan_enable_timing", "rnn_plan_last_timings", "rnn_plan_describe",
             "rnn_plan_destroy", "rnn_last_error"]
 
@@ -84,6 +85,8 @@ def load() -> ctypes.CDLL:
     L.rnn_run.restype = i32
     L.rnn_run.argtypes = [vp, vp, vp, sz, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_int32),
                           vp, vp, vp, vp, vp, vp]
+    L.rnn_cell_run.restype = i32
+    L.rnn_cell_run.argtypes = [vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.rnn_workspace_check.restype = i32
     L.rnn_workspace_check.argtypes = [vp, vp, vp]
     L.rnn_plan_enable_timing.restype = i32

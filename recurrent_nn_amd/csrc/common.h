@@ -44,6 +44,7 @@ struct Layout {
     size_t zbuf = 0;    // GRU lbr=0 update gate between launches [D][Bt][H]
     size_t lens = 0;    // int32 [Bt]
     size_t bar = 0;     // uint32 step flags [D*NBB][2][NUB], then int32 error word
+    size_t cellb = 0;   // rnn_cell_run: summed biases expanded to [D][Wb = sum, Rb = 0]
     size_t total = 0;
 };
 
@@ -184,5 +185,7 @@ struct FinalArgs {
     int64_t n;              // D * Bt * H
 };
 int launch_zero_size_states(const FinalArgs &a, void *stream);
+// dst[d][0, GH) = B_sum[d][...], dst[d][GH, 2 GH) = +0 for d < D
+int launch_cell_bias(const float *B_sum, float *dst, int64_t D, int64_t GH, void *stream);
 
 }  // namespace rnnamd

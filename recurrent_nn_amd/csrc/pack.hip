@@ -206,6 +206,33 @@ __global__ void zero_size_states(FinalArgs a)
     }
 }
 
+// The cell convention's single summed bias B (OpenVINO "RNNCell-3", section
+// "Inputs": the sum of the W and R biases) as an ONNX B: Wb = B, Rb = +0.
+// Adding +0 after it is exact: no pre-activation is -0 at that point (both
+// products' sums start at +0).
+__global__ void cell_bias_kernel(const float *__restrict__ Bs, float *__restrict__ dst, int64_t D,
+                                 int64_t GH)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < D * 2 * GH;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t d = i / (2 * GH), k = i - d * 2 * GH;
+        dst[i] = k < GH ? Bs[d * GH + k] : 0.0f;
+    }
+}
+
+int launch_cell_bias(const float *B_sum, float *dst, int64_t D, int64_t GH, void *stream)
+{
+    const int64_t n = D * 2 * GH;
+    if (n <= 0)
+        return 0;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 1024)
+        blocks = 1024;
+    hipLaunchKernelGGL(cell_bias_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       B_sum, dst, D, GH);
+    return (int)hipGetLastError();
+}
+
 int launch_zero_size_states(const FinalArgs &a, void *stream)
 {
     if (a.n <= 0)

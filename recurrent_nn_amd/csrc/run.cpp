@@ -126,20 +126,14 @@ rnn_status device_setup(rnn_plan *p, unsigned char *ws)
     return RNN_OK;
 }
 
-}  // namespace
 
-extern "C" rnn_status rnn_run(rnn_plan *p, void *hip_stream, void *workspace, size_t workspace_bytes,
-                              const float *X, const float *W, const float *R, const float *B,
-                              const int32_t *sequence_lens, const float *initial_h,
-                              const float *initial_c, const float *P, float *Y, float *Y_h,
-                              float *Y_c)
+// Every argument check of a run; nothing is enqueued.
+rnn_status run_checks(const rnn_plan *p, const void *workspace, size_t workspace_bytes,
+                      const float *X, const float *W, const float *R, const float *B,
+                      const int32_t *sequence_lens, const float *initial_h,
+                      const float *initial_c, const float *P, const float *Y, const float *Y_h,
+                      const float *Y_c)
 {
-    set_error("");
-    if (!p) {
-        set_error("rnn_run: NULL plan");
-        return RNN_ERR_INVALID_INPUT;
-    }
-    hipStream_t s = (hipStream_t)hip_stream;
     const bool zero = p->S == 0 || p->Bt == 0;
     if (p->op != RNN_OP_LSTM && (initial_c || P || Y_c)) {
         set_error("rnn_run: initial_c, P and Y_c are LSTM-only");
@@ -167,16 +161,24 @@ extern "C" rnn_status rnn_run(rnn_plan *p, void *hip_stream, void *workspace, si
                 return RNN_ERR_INVALID_INPUT;
             }
 
-    if (zero) {
-        FinalArgs f{initial_h, initial_c, Y_h, Y_c, (int64_t)p->D * p->Bt * p->H};
-        int rc = launch_zero_size_states(f, s);
-        return rc ? hip_fail((hipError_t)rc, "zero-size state copy") : RNN_OK;
-    }
-
-    if (!workspace || workspace_bytes < p->ws.total || !aligned(workspace, 256)) {
+    if (!zero && (!workspace || workspace_bytes < p->ws.total || !aligned(workspace, 256))) {
         set_error("rnn_run: workspace missing, smaller than rnn_plan_workspace_size() or not "
                   "256-byte aligned");
         return RNN_ERR_INVALID_INPUT;
+    }
+    return RNN_OK;
+}
+
+// The launch sequence of a checked run.
+rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float *X,
+                       const float *W, const float *R, const float *B,
+                       const int32_t *sequence_lens, const float *initial_h,
+                       const float *initial_c, const float *P, float *Y, float *Y_h, float *Y_c)
+{
+    if (p->S == 0 || p->Bt == 0) {
+        FinalArgs f{initial_h, initial_c, Y_h, Y_c, (int64_t)p->D * p->Bt * p->H};
+        int rc = launch_zero_size_states(f, s);
+        return rc ? hip_fail((hipError_t)rc, "zero-size state copy") : RNN_OK;
     }
     unsigned char *ws = (unsigned char *)workspace;
     rnn_status st = device_setup(p, ws);
@@ -287,6 +289,71 @@ extern "C" rnn_status rnn_run(rnn_plan *p, void *hip_stream, void *workspace, si
     }
     tm.end(STAGE_REC);
     return RNN_OK;
+}
+
+}  // namespace
+
+extern "C" rnn_status rnn_run(rnn_plan *p, void *hip_stream, void *workspace, size_t workspace_bytes,
+                              const float *X, const float *W, const float *R, const float *B,
+                              const int32_t *sequence_lens, const float *initial_h,
+                              const float *initial_c, const float *P, float *Y, float *Y_h,
+                              float *Y_c)
+{
+    set_error("");
+    if (!p) {
+        set_error("rnn_run: NULL plan");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    rnn_status st = run_checks(p, workspace, workspace_bytes, X, W, R, B, sequence_lens, initial_h,
+                               initial_c, P, Y, Y_h, Y_c);
+    if (st != RNN_OK)
+        return st;
+    return run_enqueue(p, (hipStream_t)hip_stream, workspace, X, W, R, B, sequence_lens, initial_h,
+                       initial_c, P, Y, Y_h, Y_c);
+}
+
+extern "C" rnn_status rnn_cell_run(rnn_plan *p, void *hip_stream, void *workspace,
+                                   size_t workspace_bytes, const float *X, const float *H,
+                                   const float *C, const float *W, const float *R,
+                                   const float *B_sum, const float *P, float *H_out, float *C_out)
+{
+    set_error("");
+    if (!p) {
+        set_error("rnn_cell_run: NULL plan");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    if (p->S != 1 || p->D != 1) {
+        set_error("rnn_cell_run: the plan must have seq_length 1 and one direction");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    if (!H_out && p->Bt > 0) {
+        set_error("rnn_cell_run: H_out is required");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    if (B_sum && p->op == RNN_OP_GRU && p->lbr) {
+        set_error("rnn_cell_run: a summed bias cannot express GRU with linear_before_reset = 1 "
+                  "(its recurrent candidate bias is scaled by the reset gate)");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    if (B_sum && !aligned(B_sum, 4)) {
+        set_error("rnn_run: tensors must be 4-byte aligned");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    // the expanded bias lives in the workspace; checked as rnn_run checks it
+    const float *B = nullptr;
+    if (B_sum && p->Bt > 0 && workspace)
+        B = (const float *)((unsigned char *)workspace + p->ws.cellb);
+    rnn_status st = run_checks(p, workspace, workspace_bytes, X, W, R, B, nullptr, H, C, P,
+                               nullptr, H_out, C_out);
+    if (st != RNN_OK)
+        return st;
+    hipStream_t s = (hipStream_t)hip_stream;
+    if (B) {
+        int rc = launch_cell_bias(B_sum, (float *)B, p->D, (int64_t)p->G * p->H, s);
+        if (rc)
+            return hip_fail((hipError_t)rc, "summed-bias expansion");
+    }
+    return run_enqueue(p, s, workspace, X, W, R, B, nullptr, H, C, P, nullptr, H_out, C_out);
 }
 
 extern "C" rnn_status rnn_workspace_check(const rnn_plan *p, void *hip_stream, const void *workspace)

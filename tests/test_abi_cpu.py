@@ -129,6 +129,39 @@ def test_run_time_errors_before_any_device_work():
     assert ra.rnn_run(0, 0, fake, ws, fake, fake, fake) == ra.RNN_ERR_INVALID_INPUT
 
 
+def test_cell_run_errors_before_any_device_work():
+    fake = 1 << 20          # a 256-aligned address that is never dereferenced
+    # a plan with more than one step or direction is not a cell plan
+    p = ra.RNNPlan("RNN", 2, 3, 8, 16)
+    st = ra.rnn_cell_run(p.plan, 0, fake, p.workspace_bytes, fake, 0, 0, fake, fake, 0, 0, fake, 0)
+    assert st == ra.RNN_ERR_INVALID_INPUT and "seq_length 1" in ra.rnn_last_error()
+    p = ra.RNNPlan("RNN", 1, 3, 8, 16, direction="bidirectional")
+    st = ra.rnn_cell_run(p.plan, 0, fake, p.workspace_bytes, fake, 0, 0, fake, fake, 0, 0, fake, 0)
+    assert st == ra.RNN_ERR_INVALID_INPUT
+    c = ra.RNNCell("GRU", 3, 8, 16, linear_before_reset=1)
+    ws = c.workspace_bytes
+    # a summed bias cannot carry GRU's reset-after-product candidate bias
+    st = ra.rnn_cell_run(c.plan, 0, fake, ws, fake, 0, 0, fake, fake, fake, 0, fake, 0)
+    assert st == ra.RNN_ERR_INVALID_INPUT and "linear_before_reset" in ra.rnn_last_error()
+    c = ra.RNNCell("LSTM", 3, 8, 16)
+    ws = c.workspace_bytes
+    # H_out required; rnn_run's checks apply (X, W, R required; workspace size)
+    assert ra.rnn_cell_run(c.plan, 0, fake, ws, fake, 0, 0, fake, fake, fake, 0, 0, 0) == \
+        ra.RNN_ERR_INVALID_INPUT
+    assert ra.rnn_cell_run(c.plan, 0, fake, ws, 0, 0, 0, fake, fake, fake, 0, fake, 0) == \
+        ra.RNN_ERR_INVALID_INPUT
+    assert ra.rnn_cell_run(c.plan, 0, fake, ws - 1, fake, 0, 0, fake, fake, fake, 0, fake, 0) == \
+        ra.RNN_ERR_INVALID_INPUT
+    assert ra.rnn_cell_run(c.plan, 0, fake, ws, fake, 0, 0, fake, fake, fake + 2, 0, fake, 0) == \
+        ra.RNN_ERR_INVALID_INPUT
+    assert ra.rnn_cell_run(0, 0, fake, ws, fake, 0, 0, fake, fake, 0, 0, fake, 0) == \
+        ra.RNN_ERR_INVALID_INPUT
+    # C / P / C_out are LSTM-only
+    r = ra.RNNCell("RNN", 3, 8, 16)
+    assert ra.rnn_cell_run(r.plan, 0, fake, r.workspace_bytes, fake, 0, 0, fake, fake, 0, 0, fake,
+                           fake) == ra.RNN_ERR_INVALID_INPUT
+
+
 def test_workspace_and_tiling_of_the_named_workloads():
     expect = {
         "lstm_bidir_s512_b64_i1024_h1024": dict(resident="1", workgroups="256"),

@@ -182,6 +182,57 @@ def test_rnn_single_step_is_the_rnncell_formula():
     assert np.abs(Yh[0] - ho).max() < 2e-6
 
 
+@pytest.mark.parametrize("act", ["Tanh", "Relu", "Sigmoid"])
+def test_cell_convention_matches_the_rnncell_closed_form(act):
+    # OpenVINO RNNCell-3: Ho = f(X Wi^T + H Ri^T + B), B the summed bias,
+    # f one of relu / sigmoid / tanh ("Attributes"); written out in fp64.
+    rs = np.random.RandomState(7)
+    Bn, I, H = 3, 5, 4
+    x = rs.uniform(-1, 1, (Bn, I)).astype(np.float32)
+    h = rs.uniform(-1, 1, (Bn, H)).astype(np.float32)
+    W = rs.uniform(-0.5, 0.5, (H, I)).astype(np.float32)
+    R = rs.uniform(-0.5, 0.5, (H, H)).astype(np.float32)
+    Bs = rs.uniform(-0.5, 0.5, (H,)).astype(np.float32)
+    pre = (x.astype(np.float64) @ W.T.astype(np.float64) + h.astype(np.float64) @ R.T.astype(np.float64)
+           + Bs.astype(np.float64))
+    f = {"Tanh": np.tanh, "Relu": lambda v: np.maximum(v, 0.0),
+         "Sigmoid": lambda v: 1.0 / (1.0 + np.exp(-v))}[act]
+    ho, co = oracle.run_cell("RNN", x, W, R, Bs, H=h, activations=[act])
+    assert co is None and ho.shape == (Bn, H)
+    assert np.abs(ho - f(pre)).max() < 2e-6
+    # no H: the previous state is zero; no B: no bias
+    ho0, _ = oracle.run_cell("RNN", x, W, R, None, activations=[act])
+    assert np.abs(ho0 - f(x.astype(np.float64) @ W.T.astype(np.float64))).max() < 2e-6
+
+
+@pytest.mark.parametrize("op,attrs", [("GRU", dict(linear_before_reset=0)), ("LSTM", {}),
+                                      ("LSTM", dict(with_p=True))])
+def test_cell_convention_of_gru_and_lstm_matches_fp64_brute_force(op, attrs):
+    # the summed bias on every gate: Wb = B_sum, Rb = 0 in the operator's
+    # formulas, checked against the fp64 restatement at seq 1
+    a = dict(attrs)
+    with_p = a.pop("with_p", False)
+    c = workloads.random_case(op, "forward", 1, 4, 6, 5, seed=31, with_h0=True,
+                              with_c0=(op == "LSTM"), with_p=with_p, **a)
+    G = {"GRU": 3, "LSTM": 4}[op]
+    Bs = c.B[0, :G * 5].clone()
+    c.B = torch.cat([Bs, torch.zeros(G * 5)])[None]
+    ref = brute64.run(c)
+    ho, co = oracle.run_cell(op, c.X[0], c.W[0], c.R[0], Bs, H=c.initial_h[0],
+                             C=None if c.initial_c is None else c.initial_c[0],
+                             P=None if c.P is None else c.P[0], **a)
+    assert np.abs(ho - ref[1][0]).max() < 3e-6
+    if op == "LSTM":
+        assert np.abs(co - ref[2][0]).max() < 3e-6
+
+
+def test_cell_convention_refuses_a_summed_bias_for_gru_reset_after_product():
+    x = np.zeros((1, 2), np.float32)
+    with pytest.raises(ValueError):
+        oracle.run_cell("GRU", x, np.zeros((9, 2), np.float32), np.zeros((9, 3), np.float32),
+                        np.zeros(9, np.float32), linear_before_reset=1)
+
+
 # ---------------------------------------------------------------------------
 # Operation order: cases whose answer depends on the written order
 # ---------------------------------------------------------------------------
