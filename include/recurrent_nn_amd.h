@@ -109,6 +109,12 @@ typedef struct rnn_attrs {
                                           RNN, LSTM or GRU with linear_before_reset = 1, and
                                           a batch tile of 32 or 64; else InvalidInput).
                                           Results are identical either way.              */
+    int32_t time_chunk;                /* 0 = all steps at once; else steps per chunk: the
+                                          projections and the H history are held for one
+                                          chunk at a time and the states carry over between
+                                          chunks, so the scratch limit applies to the chunk
+                                          length instead of seq_length.  Results are
+                                          identical either way.                          */
 } rnn_attrs;
 
 /* Dimensions: hidden is R's last dimension, num_directions W's first. */
@@ -130,9 +136,10 @@ typedef struct rnn_plan rnn_plan;
  *   Errors: RNN_ERR_INVALID_INPUT (unknown op/direction/activation name, wrong
  *   activation count, num_directions not matching direction, layout not 0/1,
  *   hidden 0 or not equal to hidden_size, input_forget on a non-LSTM,
- *   linear_before_reset on a non-GRU, negative sizes); RNN_ERR_UNSUPPORTED
- *   when, per direction, seq*batch*G*hidden + 4*batch*hidden (+ G*hidden*
- *   (input+hidden) unless constant_weights) reaches 2^30 floats.
+ *   linear_before_reset on a non-GRU, negative sizes or time_chunk);
+ *   RNN_ERR_UNSUPPORTED when, per direction, L*batch*G*hidden + 4*batch*hidden
+ *   (+ G*hidden*(input+hidden) unless constant_weights) reaches 2^30 floats,
+ *   with L = seq_length, or the chunk length when time_chunk is set.
  */
 rnn_status rnn_plan_create(const rnn_attrs *attrs, const rnn_dims *dims, rnn_plan **out);
 

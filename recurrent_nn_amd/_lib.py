@@ -50,6 +50,7 @@ class rnn_attrs(ctypes.Structure):
         ("waves_per_block", ctypes.c_int32),
         ("barrier_spin_limit", ctypes.c_int32),
         ("batch_halves", ctypes.c_int32),
+        ("time_chunk", ctypes.c_int32),
     ]
 
 

@@ -36,13 +36,14 @@ constexpr uint32_t kDefaultSpinLimit = 1u << 26;   // ~seconds of polling: a ste
 struct Layout {
     size_t wp = 0;      // packed W: rows in block-column order, [D*G*H][I] f32 or bf16
     size_t rp = 0;      // packed R: [D][NUB][NT*16][Hp] f32, zero-padded
-    size_t xb = 0;      // X rounded to bf16 (bf16 projection only): [S*Bt][I]
-    size_t xw = 0;      // projections: [D][S][Bt][G*H] f32, block-column order
-    size_t hbuf = 0;    // H history: plane j = H before step j, [S+1][D][Btp][Hp] f32
-    size_t sbuf = 0;    // GRU lbr=0: r (.) H_prev of step j in plane j, [S][D][Btp][Hp]
+    size_t xb = 0;      // bf16 projection: the chunk's X rows by step, rounded, [D][C*Bt][I]
+    size_t xw = 0;      // projections: [D][C][Bt][G*H] f32 by step, block-column order
+    size_t hbuf = 0;    // H history: plane j mod (C+1) = H before step j, [C+1][D][Btp][Hp] f32
+    size_t sbuf = 0;    // GRU lbr=0: r (.) H_prev of step j in plane j mod C, [C][D][Btp][Hp]
     size_t cbuf = 0;    // LSTM cell state between launches [D][Bt][H]
     size_t zbuf = 0;    // GRU lbr=0 update gate between launches [D][Bt][H]
     size_t lens = 0;    // int32 [Bt]
+    size_t order = 0;   // int32 [Bt]: batch rows by decreasing sequence length
     size_t bar = 0;     // uint32 step flags [D*NBB][2][NUB], then int32 error word
     size_t cellb = 0;   // rnn_cell_run: summed biases expanded to [D][Wb = sum, Rb = 0]
     size_t total = 0;
@@ -67,6 +68,7 @@ struct rnn_plan {
     uint32_t spin_limit = 0;  // polls before a step barrier gives up
     int32_t withhold_flags = 0;   // test fault injection: step flags are never stored
     int64_t S = 0, Bt = 0, I = 0, H = 0;
+    int64_t C = 0;            // steps per chunk (time_chunk; S when not chunked)
     rnnamd::ActSpec act[2][3] = {};
 
     // tiling of the recurrence
@@ -100,6 +102,12 @@ struct rnn_plan {
     int32_t device = -1;
 
     // timing
+    // pinned host staging of sequence_lens and their order (copied to the
+    // device asynchronously; the event guards its reuse by the next run)
+    int32_t *lens_host = nullptr;
+    void *lens_event = nullptr;
+    int32_t lens_pending = 0;
+
     int32_t timing = 0;
     void *events[2 * rnnamd::STAGE_COUNT] = {};
     int32_t events_recorded = 0;
@@ -127,7 +135,6 @@ struct PackArgs {
 };
 int launch_pack(const PackArgs &a, void *stream);
 
-int launch_cast_bf16(const float *X, uint16_t *Xb, int64_t n, void *stream);
 
 struct InitArgs {
     const float *h0, *c0;       // nullable, layout-dependent
@@ -142,12 +149,18 @@ struct InitArgs {
 int launch_init(const InitArgs &a, void *stream);
 
 struct ProjArgs {
-    const void *X;          // f32 [M][I] or bf16
-    const void *Wp;         // f32 [N][I] or bf16
-    float *XW;              // [D][S][Bt][GH]
-    int64_t M, N, K;        // M = S*Bt, N = D*G*H, K = I
-    int64_t S, Bt, GH;
-    int32_t layout;         // row remap of layout 1
+    const void *X;          // f32 X in the operator's layout
+    uint16_t *Xb;           // bf16 projection: [D][steps * Bt][K] staging of the gathered rows
+    const void *Wp;         // f32 or bf16 packed W, [D][GH][I]
+    float *XW;              // [D][steps][Bt][GH], row (j - j_base, b) of direction d
+    int64_t K;              // I
+    int64_t S, Bt, GH, D;
+    int64_t steps;          // steps held by XW (the chunk length)
+    int64_t j_base;         // first step of the chunk
+    const int32_t *lens;    // [Bt] on the device
+    const int32_t *order;   // [Bt] batch rows by decreasing length, or NULL (identity)
+    int32_t reverse_only;   // direction 0 runs in reverse
+    int32_t layout;         // 0: X [S][Bt][I]; 1: X [Bt][S][I]
     int32_t bf16;
 };
 int launch_projection(const ProjArgs &a, void *stream);
@@ -172,6 +185,11 @@ struct RecArgs {
     int32_t withhold_flags;  // test fault injection: never store the step flags
     // launch range in phase units (step j, phase p) -> q = j * phases + p
     int32_t q_begin, q_end;
+    // time chunk of xw_steps steps starting at j_base: XW row = j - j_base;
+    // the H history is a ring of xw_steps + 1 planes (plane j mod (steps+1)),
+    // r (.) H_prev a ring of xw_steps planes, so one chunk's last plane is the
+    // next chunk's first and every plane is fresh within a launch
+    int32_t j_base, xw_steps;
 };
 // persistent: one cooperative launch covering every phase; else one phase.
 int launch_recurrence(const RecArgs &a, int resident, int persistent, void *stream);

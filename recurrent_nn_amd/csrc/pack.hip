@@ -118,25 +118,6 @@ int launch_pack(const PackArgs &a, void *stream)
 
 // X -> bf16 (round to nearest even); kept for callers that want a separate
 // cast (the projection kernel otherwise rounds X while staging it).
-__global__ void cast_bf16_kernel(const float *__restrict__ X, uint16_t *__restrict__ Xb, int64_t n)
-{
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x)
-        Xb[i] = bf16_rne(X[i]);
-}
-
-int launch_cast_bf16(const float *X, uint16_t *Xb, int64_t n, void *stream)
-{
-    if (n <= 0)
-        return 0;
-    int64_t blocks = (n + 255) / 256;
-    if (blocks > 65536)
-        blocks = 65536;
-    hipLaunchKernelGGL(cast_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                       (hipStream_t)stream, X, Xb, n);
-    return (int)hipGetLastError();
-}
-
 // States before the first step: plane 0 of the H history holds initial_h
 // (zero when absent, and zero in the padding rows and columns), cbuf holds
 // initial_c, and the step flags and the error word are cleared.  Later planes

@@ -286,13 +286,13 @@ void make_layout(rnn_plan &p)
     const size_t wsz = p.proj_bf16 ? 2 : 4;
     L.wp = take((size_t)p.D * GH * p.I * wsz);
     L.rp = take((size_t)p.D * p.NUB * p.NT * 16 * p.Hp * 4);
-    L.xb = take(0);   // X is rounded to bf16 inside the projection's staging
-    L.xw = take((size_t)p.D * p.S * p.Bt * GH * 4);
-    L.hbuf = take((size_t)(p.S + 1) * p.D * p.Btp * p.Hp * 4);
-    L.sbuf = take(p.phases == 2 ? (size_t)p.S * p.D * p.Btp * p.Hp * 4 : 0);
+    L.xb = take(p.proj_bf16 ? (size_t)p.D * p.C * p.Bt * p.I * 2 : 0);
+    L.xw = take((size_t)p.D * p.C * p.Bt * GH * 4);
+    L.hbuf = take((size_t)(p.C + 1) * p.D * p.Btp * p.Hp * 4);
+    L.sbuf = take(p.phases == 2 ? (size_t)p.C * p.D * p.Btp * p.Hp * 4 : 0);
     L.cbuf = take(p.op == RNN_OP_LSTM ? (size_t)p.D * p.Bt * p.H * 4 : 0);
     L.zbuf = take(p.phases == 2 ? (size_t)p.D * p.Bt * p.H * 4 : 0);
-    L.lens = take((size_t)std::max<int64_t>(p.Bt, 1) * 4);
+    L.lens = take((size_t)std::max<int64_t>(p.Bt, 1) * 2 * 4);   // lengths, then their order
     L.bar = take((size_t)(n_flags(p) + 1) * 4);
     L.cellb = take((size_t)p.D * 2 * GH * 4);
     L.total = off;
@@ -371,6 +371,9 @@ extern "C" rnn_status rnn_plan_create(const rnn_attrs *attrs, const rnn_dims *di
     p->proj_bf16 = a.proj_dtype == RNN_PROJ_BF16;
     p->constant_weights = a.constant_weights ? 1 : 0;
     p->kernel_path = a.kernel_path;
+    if (a.time_chunk < 0)
+        return fail(RNN_ERR_INVALID_INPUT, "time_chunk must be >= 0");
+    p->C = (a.time_chunk > 0 && a.time_chunk < p->S) ? a.time_chunk : p->S;
     if (a.barrier_spin_limit < 0)
         return fail(RNN_ERR_INVALID_INPUT, "barrier_spin_limit must be >= 0");
     p->spin_limit = a.barrier_spin_limit ? (uint32_t)a.barrier_spin_limit : kDefaultSpinLimit;
@@ -387,8 +390,10 @@ extern "C" rnn_status rnn_plan_create(const rnn_attrs *attrs, const rnn_dims *di
         return fail(st, "");
 
     // Limits: per direction, seq*batch*G*H + 4*batch*H (+ transposed weights
-    // when not constant) floats must stay below 2^30.
-    double need = (double)p->S * (double)p->Bt * p->G * (double)p->H + 4.0 * (double)p->Bt * p->H;
+    // when not constant) floats must stay below 2^30.  With time chunks the
+    // projections held at once are those of one chunk: seq becomes the chunk
+    // length (the limit the chunked form lifts).
+    double need = (double)p->C * (double)p->Bt * p->G * (double)p->H + 4.0 * (double)p->Bt * p->H;
     if (!p->constant_weights)
         need += (double)p->G * p->H * ((double)p->I + (double)p->H);
     if (!(need < 1073741824.0))
@@ -423,10 +428,11 @@ extern "C" rnn_status rnn_plan_describe(const rnn_plan *p, char *buf, size_t len
         return RNN_ERR_INVALID_INPUT;
     }
     std::snprintf(buf, len,
-                  "op=%d G=%d D=%d S=%lld Bt=%lld I=%lld H=%lld U=%d NUB=%d BT=%d NBB=%d MT=%d "
-                  "NTA=%d NTB=%d phases=%d Hp=%lld waves=%d KB=%d resident=%d halves=%d workgroups=%d "
-                  "path=%d persist=%d ws=%zu",
-                  p->op, p->G, p->D, (long long)p->S, (long long)p->Bt, (long long)p->I,
+                  "op=%d G=%d D=%d S=%lld C=%lld Bt=%lld I=%lld H=%lld U=%d NUB=%d BT=%d NBB=%d "
+                  "MT=%d NTA=%d NTB=%d phases=%d Hp=%lld waves=%d KB=%d resident=%d halves=%d "
+                  "workgroups=%d path=%d persist=%d ws=%zu",
+                  p->op, p->G, p->D, (long long)p->S, (long long)p->C, (long long)p->Bt,
+                  (long long)p->I,
                   (long long)p->H, p->U, p->NUB, p->BT, p->NBB, p->MT, p->NTA, p->NTB, p->phases,
                   (long long)p->Hp, p->NW, p->KB, p->resident, p->halves, p->n_wg, p->kernel_path,
                   p->can_persist, p->ws.total);

@@ -1,14 +1,23 @@
 // proj_gemm.hip -- the input projection XW = X . W^T over all time steps
 // (onemodel "Recurrent operators", section "Computation", step 1: one matrix
-// product of shape [seq*batch, G*H] per direction).  Both directions are one
-// product with N = dirs*G*H; W arrives packed (rows in block-column order,
-// see pack.hip), so XW comes out in the order the recurrence reads it.
+// product of shape [seq*batch, G*H] per direction).  W arrives packed (rows
+// in block-column order, see pack.hip), so XW comes out in the order the
+// recurrence reads it.
+//
+// Rows.  XW is stored by STEP: row (j - j_base, b) of direction d holds the
+// projection of the X row that step j of batch row b reads -- time j
+// forward, len_b - 1 - j in reverse ("Choices the specification leaves
+// open": sequence_lens and reverse traversal) -- for the steps of one time
+// chunk.  Rows the step loop never reads (j >= len_b) are not computed: a
+// tile whose rows are all such is skipped, and batch rows are visited in
+// order of decreasing length so that they cluster.  Both directions are one
+// launch (the direction is part of the tile index).
 //
 // Tiling: 128x128 output tile per 256-thread workgroup, 4 waves of 64x64, K
 // staged through LDS in 128-byte row slices (32 fp32 or 64 bf16 values) with
 // double buffering.  fp32 uses v_mfma_f32_16x16x4_f32, bf16 uses the gfx950
-// v_mfma_f32_16x16x32_bf16; for bf16, X is rounded to bfloat16 (nearest even)
-// while it is staged, so no separate cast pass runs.  Accumulation is in the
+// v_mfma_f32_16x16x32_bf16; for bf16, the chunk's X rows are first gathered
+// and rounded to bfloat16 (nearest even) once by gather_bf16_kernel.  Accumulation is in the
 // matrix cores' order with a fixed tiling (deterministic, "fast mode").
 //
 // Each lane feeds the matrix core 16 contiguous bytes of one row per 16x16
@@ -40,12 +49,13 @@ __device__ __forceinline__ uint32_t bf16_bits(float f)
     return u >> 16;
 }
 
-// 4 fp32 values of row `row` at k .. k+3, zero outside [0, rows) x [0, K).
+// 4 fp32 values of row `row` at k .. k+3, zero for row < 0 or row >= rows
+// and outside [0, K).
 __device__ __forceinline__ f4 load4(const float *__restrict__ p, int64_t row, int64_t k,
                                     int64_t rows, int64_t K, bool vec_ok)
 {
     f4 v = {0.f, 0.f, 0.f, 0.f};
-    if (row >= rows)
+    if (row < 0 || row >= rows)
         return v;
     const float *q = p + row * K + k;
     if (vec_ok && k + 3 < K)
@@ -88,6 +98,51 @@ __device__ __forceinline__ u4 pack8(f4 a, f4 b)
     return v;
 }
 
+// X row read by logical row m = (j - j_base) * Bt + i of direction d, i.e.
+// step j of batch row order[i]; -1 when the step loop never reads it
+// (j >= len) or m is past the chunk.
+__device__ __forceinline__ int64_t proj_xrow(const ProjArgs &a, int64_t d, int64_t m)
+{
+    if (m >= a.steps * a.Bt)
+        return -1;
+    const uint32_t jl = (uint32_t)m / (uint32_t)a.Bt, i = (uint32_t)m - jl * (uint32_t)a.Bt;
+    const int64_t b = a.order ? a.order[i] : i;
+    const int64_t j = a.j_base + jl, len = a.lens[b];
+    if (j >= len)
+        return -1;
+    const int64_t t = (a.reverse_only || d == 1) ? len - 1 - j : j;
+    return a.layout == 0 ? t * a.Bt + b : b * a.S + t;
+}
+
+// bf16 projection: the chunk's X rows in step order, rounded to bfloat16
+// (nearest even) once, zeros for rows never read; the product then reads
+// bf16 rows directly instead of converting in every N tile.
+__global__ void gather_bf16_kernel(ProjArgs a)
+{
+    const int64_t Md = a.steps * a.Bt;
+    const float *X = (const float *)a.X;
+    const bool vec = a.K % 8 == 0;
+    for (int64_t row = blockIdx.x; row < a.D * Md; row += gridDim.x) {
+        const int64_t d = row / Md, m = row - d * Md;
+        const int64_t xr = proj_xrow(a, d, m);
+        uint16_t *dst = a.Xb + row * a.K;
+        const float *src = xr >= 0 ? X + xr * a.K : nullptr;
+        if (vec) {
+            for (int64_t k = threadIdx.x * 8; k < a.K; k += blockDim.x * 8) {
+                f4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+                if (src) {
+                    x0 = *(const f4 *)(src + k);
+                    x1 = *(const f4 *)(src + k + 4);
+                }
+                *(u4 *)(dst + k) = pack8(x0, x1);
+            }
+        } else {
+            for (int64_t k = threadIdx.x; k < a.K; k += blockDim.x)
+                dst[k] = src ? (uint16_t)bf16_bits(src[k]) : (uint16_t)0;
+        }
+    }
+}
+
 // Tile order: workgroups on one XCD (blockIdx % 8) take a contiguous range
 // of tiles, walked in bands of GM tile-rows so that neighbours share panels.
 __device__ __forceinline__ void tile_of(int64_t wg, int64_t nwg, int64_t tiles_m, int64_t tiles_n,
@@ -115,10 +170,13 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs a)
     const int lr = lane & 15, lq = lane >> 4;
     const int wm = w >> 1, wn = w & 1;
 
-    const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
-    int64_t tm, tn;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
+    const int64_t Md = a.steps * a.Bt;                 // rows per direction
+    const int64_t tiles_m = (Md + BM - 1) / BM, tiles_n = (a.GH + BN - 1) / BN;
+    int64_t tmg, tn;
+    tile_of(blockIdx.x, gridDim.x, a.D * tiles_m, tiles_n, &tmg, &tn);
+    const int64_t d = tmg / tiles_m, tm = tmg - d * tiles_m;
     const int64_t m0 = tm * BM, n0 = tn * BN;
+    const int64_t xrows = a.S * a.Bt;
 
     // k values per stage: 32 (fp32) or 64 (bf16)
     constexpr int KS = BF16 ? 64 : 32;
@@ -128,6 +186,16 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs a)
 
     // staging: thread -> (row = tid / 8 + 32 i, chunk = tid % 8 of 16 bytes)
     const int srow = tid >> 3, sch = tid & 7;
+    int64_t xr[4];
+    int any = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        xr[i] = proj_xrow(a, d, m0 + srow + 32 * i);
+        any |= xr[i] >= 0;
+    }
+    if (!__syncthreads_or(any))
+        return;                                      // no row of this tile is ever read
+    const char *Wd = (const char *)a.Wp + (size_t)d * a.GH * a.K * (BF16 ? 2 : 4);
     u4 ra[4], rb[4];
     auto gload = [&](int64_t kt, u4 (&ra)[4], u4 (&rb)[4]) {
         const int64_t kbase = kt * KS;
@@ -135,16 +203,13 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs a)
         for (int i = 0; i < 4; ++i) {
             const int64_t row = srow + 32 * i;
             if constexpr (BF16) {
-                const float *X = (const float *)a.X;
                 const int64_t k = kbase + sch * 8;
-                f4 x0 = load4(X, m0 + row, k, a.M, a.K, a_vec);
-                f4 x1 = load4(X, m0 + row, k + 4, a.M, a.K, a_vec);
-                ra[i] = pack8(x0, x1);
-                rb[i] = load8h((const uint16_t *)a.Wp, n0 + row, k, a.N, a.K, b_vec);
+                ra[i] = load8h(a.Xb + (size_t)d * Md * a.K, m0 + row, k, Md, a.K, b_vec);
+                rb[i] = load8h((const uint16_t *)Wd, n0 + row, k, a.GH, a.K, b_vec);
             } else {
                 const int64_t k = kbase + sch * 4;
-                f4 x = load4((const float *)a.X, m0 + row, k, a.M, a.K, a_vec);
-                f4 y = load4((const float *)a.Wp, n0 + row, k, a.N, a.K, b_vec);
+                f4 x = load4((const float *)a.X, xr[i], k, xrows, a.K, a_vec);
+                f4 y = load4((const float *)Wd, n0 + row, k, a.GH, a.K, b_vec);
                 ra[i] = __builtin_bit_cast(u4, x);
                 rb[i] = __builtin_bit_cast(u4, y);
             }
@@ -211,52 +276,47 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs a)
         __syncthreads();
     }
 
-    // store: lane holds rows 4*lq + r, column lr of each 16x16 tile.  The
-    // direction of a column and the row permutation of layout 1 are resolved
-    // once per column / row (32-bit divisions: M, N < 2^31 here).
-    size_t colbase[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t n = n0 + wn * 64 + j * 16 + lr;
-        const uint32_t d = n < a.N ? (uint32_t)n / (uint32_t)a.GH : 0u;
-        colbase[j] = n < a.N ? (size_t)d * a.S * a.Bt * a.GH + (size_t)(n - (int64_t)d * a.GH)
-                             : ~(size_t)0;
-    }
+    // store: lane holds rows 4*lq + r, column lr of each 16x16 tile; logical
+    // row (j - j_base, i) goes to XW row (j - j_base, order[i])
+    float *XWd = a.XW + (size_t)d * Md * a.GH;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t m = m0 + wm * 64 + i * 16 + lq * 4 + r;
-            if (m >= a.M)
+            if (m >= Md)
                 continue;
-            size_t xrow;    // row of XW[d] = t * Bt + b
-            if (a.layout == 0) {
-                xrow = (size_t)m;
-            } else {
-                const uint32_t b = (uint32_t)m / (uint32_t)a.S, t = (uint32_t)m - b * (uint32_t)a.S;
-                xrow = (size_t)t * a.Bt + b;
-            }
-            const size_t ro = xrow * a.GH;
+            const uint32_t jl = (uint32_t)m / (uint32_t)a.Bt, ii = (uint32_t)m - jl * (uint32_t)a.Bt;
+            const size_t b = a.order ? (size_t)a.order[ii] : ii;
+            const size_t ro = ((size_t)jl * a.Bt + b) * a.GH;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (colbase[j] != ~(size_t)0)
-                    a.XW[colbase[j] + ro] = acc[i][j][r];
+            for (int j = 0; j < 4; ++j) {
+                const int64_t n = n0 + wn * 64 + j * 16 + lr;
+                if (n < a.GH)
+                    XWd[ro + n] = acc[i][j][r];
+            }
         }
 }
 
 int launch_projection(const ProjArgs &a, void *stream)
 {
-    if (a.M <= 0 || a.N <= 0)
+    if (a.steps <= 0 || a.Bt <= 0 || a.GH <= 0)
         return 0;
-    const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    const int64_t tiles = a.D * ((a.steps * a.Bt + BM - 1) / BM) * ((a.GH + BN - 1) / BN);
     const size_t shmem = 2 * 2 * TILEB;
     const void *fn = a.bf16 ? (const void *)proj_gemm_kernel<true> : (const void *)proj_gemm_kernel<false>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess)
         return (int)e;
-    if (a.bf16)
+    if (a.bf16) {
+        int64_t blocks = a.D * a.steps * a.Bt;
+        if (blocks > 65536)
+            blocks = 65536;
+        hipLaunchKernelGGL(gather_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                           (hipStream_t)stream, a);
         hipLaunchKernelGGL(proj_gemm_kernel<true>, dim3((unsigned)tiles), dim3(256), shmem,
                            (hipStream_t)stream, a);
+    }
     else
         hipLaunchKernelGGL(proj_gemm_kernel<false>, dim3((unsigned)tiles), dim3(256), shmem,
                            (hipStream_t)stream, a);

@@ -314,7 +314,7 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
     const float *Wb = a.B ? a.B + (size_t)d * 2 * GH : nullptr;
     const float *Rb = a.B ? Wb + GH : nullptr;
     const float *Pd = a.P ? a.P + (size_t)d * 3 * a.H : nullptr;
-    const size_t xwd = (size_t)d * a.S * a.Bt * GH + (size_t)ub * a.G * a.U;
+    const size_t xwd = (size_t)d * a.xw_steps * a.Bt * GH + (size_t)ub * a.G * a.U;
     const int npairs = rows * uc;
 
     // R fragments: lane (lr, lq) of wave w holds R[col nt*16 + lr][k] for
@@ -335,7 +335,7 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
         for (int pi = tid; pi < npairs; pi += kThreads) {
             const int rl = pi / uc, u = pi - rl * uc;
             const int b = row0 + rl;
-            hst[pi] = a.hbuf[(size_t)j0 * plane + drow + (size_t)rl * Hp + u0 + u];
+            hst[pi] = a.hbuf[(size_t)(j0 % (a.xw_steps + 1)) * plane + drow + (size_t)rl * Hp + u0 + u];
             cst[pi] = op == RNN_OP_LSTM ? a.cbuf[((size_t)d * a.Bt + b) * a.H + u0 + u] : 0.0f;
             zst[pi] = (a.phases == 2 && (a.q_begin % 2) == 1)
                           ? a.zbuf[((size_t)d * a.Bt + b) * a.H + u0 + u]
@@ -374,8 +374,8 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
                 const int rl = pi / uc, u = pi - rl * uc;
                 const int len = lst[rl];
                 if (jj < len) {
-                    const int t = rev ? len - 1 - jj : jj;
-                    const float *src = a.XW + xwd + ((size_t)t * a.Bt + row0 + rl) * GH + u;
+                    const float *src =
+                        a.XW + xwd + ((size_t)(jj - a.j_base) * a.Bt + row0 + rl) * GH + u;
 #pragma unroll
                     for (int g = 0; g < 4; ++g)
                         if (g < a.G && ((a.phases == 2 && pp == 1) ? g == 2 : !(a.phases == 2 && g == 2)))
@@ -400,8 +400,9 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
             const int len = lst[rl];
             if (jj >= len)
                 return;
-            const int t = rev ? len - 1 - jj : jj;
-            const float *src = a.XW + xwd + ((size_t)t * a.Bt + row0 + rl) * GH + u;
+            // XW is stored by step: row (jj - j_base, b) already holds the
+            // projection of the time index this step reads (reverse included)
+            const float *src = a.XW + xwd + ((size_t)(jj - a.j_base) * a.Bt + row0 + rl) * GH + u;
             if (a.phases == 2 && pp == 1) {
                 xv[2] = src[2 * uc];
             } else {
@@ -437,7 +438,8 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
         };
 
         // ---- the product over this wave's k range --------------------------
-        const float *asrc = (ph == 0 ? a.hbuf : a.sbuf) + (size_t)j * plane + drow +
+        const float *asrc = (ph == 0 ? a.hbuf + (size_t)(j % (a.xw_steps + 1)) * plane
+                                     : a.sbuf + (size_t)(j % a.xw_steps) * plane) + drow +
                             (size_t)lr * Hp + w * KB * 16 + 4 * lq;
         f4 acc[MT][NT];
 #pragma unroll
@@ -480,8 +482,8 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
         };
 
         // ---- gate arithmetic of one (row, unit) pair, in the written order --
-        float *hnext = a.hbuf + (size_t)(j + 1) * plane + drow;
-        float *snext = a.sbuf ? a.sbuf + (size_t)j * plane + drow : nullptr;
+        float *hnext = a.hbuf + (size_t)((j + 1) % (a.xw_steps + 1)) * plane + drow;
+        float *snext = a.sbuf ? a.sbuf + (size_t)(j % a.xw_steps) * plane + drow : nullptr;
         auto do_pair = [&](int pi, const float *xv, auto F, auto Gf, auto Hf) {
             const int rl = pi / uc, u = pi - rl * uc;
             const int b = row0 + rl;

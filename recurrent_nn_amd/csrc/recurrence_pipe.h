@@ -177,7 +177,7 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
     const float *Wb = a.B ? a.B + (size_t)d * 2 * GH : nullptr;
     const float *Rb = a.B ? Wb + GH : nullptr;
     const float *Pd = a.P ? a.P + (size_t)d * 3 * a.H : nullptr;
-    const size_t xwd = (size_t)d * a.S * a.Bt * GH + (size_t)ub * a.G * a.U;
+    const size_t xwd = (size_t)d * a.xw_steps * a.Bt * GH + (size_t)ub * a.G * a.U;
     const int npairs = rows * uc;
 
     // The unit blocks whose H columns this wave's k range reads (the columns
@@ -200,7 +200,7 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
         const int j0 = a.q_begin;
         for (int pi = tid; pi < npairs; pi += 256) {
             const int rl = pi / uc, u = pi - rl * uc;
-            hst[pi] = a.hbuf[(size_t)j0 * plane + drow + (size_t)rl * Hp + u0 + u];
+            hst[pi] = a.hbuf[(size_t)(j0 % (a.xw_steps + 1)) * plane + drow + (size_t)rl * Hp + u0 + u];
             cst[pi] = op == RNN_OP_LSTM ? a.cbuf[((size_t)d * a.Bt + row0 + rl) * a.H + u0 + u] : 0.0f;
         }
         for (int rl = tid; rl < rows; rl += 256)
@@ -241,8 +241,8 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
         const int len = lst[rl];
         if (qq >= len)
             return;
-        const int t = rev ? len - 1 - qq : qq;
-        const float *src = a.XW + xwd + ((size_t)t * a.Bt + row0 + rl) * GH + u;
+        // XW is stored by step (reverse included)
+        const float *src = a.XW + xwd + ((size_t)(qq - a.j_base) * a.Bt + row0 + rl) * GH + u;
 #pragma unroll
         for (int g = 0; g < 4; ++g)
             if (g < a.G)
@@ -279,19 +279,25 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
         }
     };
 
-    // A operand of half h at step q: this wave's k range of its rows
-    auto a_src = [&](int qq, int h) {
-        return a.hbuf + (size_t)qq * plane + drow + (size_t)(h * BTH + lr) * Hp + k0 + 4 * lq;
+    // A operand of half h from H history plane `pl`: this wave's k range of
+    // its rows.  Planes form a ring of xw_steps + 1: step j reads plane
+    // j mod ring and writes the next one.
+    const int ring_n = a.xw_steps + 1;
+    auto a_src = [&](int pl, int h) {
+        return a.hbuf + (size_t)pl * plane + drow + (size_t)(h * BTH + lr) * Hp + k0 + 4 * lq;
     };
+    int pj = a.q_begin % ring_n;                 // plane of step q
+    auto next_plane = [&](int pl) { return pl + 1 == ring_n ? 0 : pl + 1; };
     constexpr int RING = (kPipePrefetch < KBR ? kPipePrefetch : KBR) + 1;
     f4 ring[RING][MTH];
     if (a.q_begin < a.q_end)
-        prime_ring<MTH, KBR, kPipePrefetch>(ring, a_src(a.q_begin, 0), Hp);
+        prime_ring<MTH, KBR, kPipePrefetch>(ring, a_src(pj, 0), Hp);
     bool primed = true;                          // the next product's first blocks are loaded
 
     for (int q = a.q_begin; q < a.q_end; ++q) {
         const int j = q;                         // one phase per step
-        float *hnext = a.hbuf + (size_t)(j + 1) * plane + drow;
+        const int pj1 = next_plane(pj);
+        float *hnext = a.hbuf + (size_t)pj1 * plane + drow;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int hrow0 = h * BTH;
@@ -303,7 +309,7 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
                 if (!dead)
                     wave_wait_flags(flags0 + (size_t)h * a.NUB + wub_lo, wub_hi - wub_lo + 1,
                                     (uint32_t)q, a.err, a.spin_limit, dead);
-                prime_ring<MTH, KBR, kPipePrefetch>(ring, a_src(q, h), Hp);
+                prime_ring<MTH, KBR, kPipePrefetch>(ring, a_src(pj, h), Hp);
             }
             float xw[P][4];
 #pragma unroll
@@ -341,7 +347,7 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
                     fv = __hip_atomic_load(nflags + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             };
             product_res_hooked<MTH, NT, KBR, kPipePrefetch, KH, KP>(
-                acc, ring, a_src(q, h), Hp, rr, prefetch_xw, publish, poll_next);
+                acc, ring, a_src(pj, h), Hp, rr, prefetch_xw, publish, poll_next);
             float *redh = red + h * 4 * BTH * LDR;
 #pragma unroll
             for (int mt = 0; mt < MTH; ++mt)
@@ -357,7 +363,7 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
             primed = !need_wait || (EARLY && nfl <= 64 && __all(fv >= (uint32_t)nq));
             asm volatile("" ::: "memory");
             if (has_next && primed)
-                prime_ring<MTH, KBR, kPipePrefetch>(ring, a_src(nq, nh), Hp);
+                prime_ring<MTH, KBR, kPipePrefetch>(ring, a_src(h == 0 ? pj : pj1, nh), Hp);
 
             // ---- gate arithmetic of this thread's pairs of half h -------------
             auto run_pairs = [&](auto F, auto Gf, auto Hf) {
@@ -424,6 +430,7 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
                 pend_gen = gens[h]++;
             }
         }
+        pj = pj1;
     }
 
     // ---- end of this launch: keep or publish the states ----------------------

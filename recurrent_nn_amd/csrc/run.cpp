@@ -8,6 +8,7 @@
 // open"); seq = 0 or batch = 0 runs nothing but the initial-state copy.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <string>
@@ -90,6 +91,8 @@ RecArgs rec_args(const rnn_plan &p, unsigned char *ws, const float *B, const flo
     r.withhold_flags = p.withhold_flags;
     r.q_begin = 0;
     r.q_end = (int32_t)(p.S * p.phases);
+    r.j_base = 0;
+    r.xw_steps = (int32_t)p.C;
     return r;
 }
 
@@ -224,11 +227,41 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
     // 2. states, exchange buffers, barrier counters, lengths
     tm.begin(STAGE_OTHER);
     int32_t *lens_dev = (int32_t *)(ws + p->ws.lens);
+    const int32_t *order_dev = nullptr;
     if (sequence_lens) {
-        e = hipMemcpyAsync(lens_dev, sequence_lens, (size_t)p->Bt * sizeof(int32_t),
+        // lengths and the batch rows in order of decreasing length (ties by
+        // row), staged in pinned memory owned by the plan
+        if (!p->lens_host) {
+            e = hipHostMalloc((void **)&p->lens_host, (size_t)p->Bt * 2 * sizeof(int32_t),
+                              hipHostMallocDefault);
+            if (e != hipSuccess)
+                return hip_fail(e, "hipHostMalloc (sequence_lens staging)");
+            hipEvent_t ev;
+            e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+            if (e != hipSuccess)
+                return hip_fail(e, "hipEventCreate");
+            p->lens_event = ev;
+        }
+        if (p->lens_pending) {
+            e = hipEventSynchronize((hipEvent_t)p->lens_event);   // the last run's copy is done
+            if (e != hipSuccess)
+                return hip_fail(e, "hipEventSynchronize (sequence_lens staging)");
+            p->lens_pending = 0;
+        }
+        int32_t *hl = p->lens_host, *ho = p->lens_host + p->Bt;
+        std::memcpy(hl, sequence_lens, (size_t)p->Bt * sizeof(int32_t));
+        for (int64_t b = 0; b < p->Bt; ++b)
+            ho[b] = (int32_t)b;
+        std::stable_sort(ho, ho + p->Bt, [hl](int32_t x, int32_t y) { return hl[x] > hl[y]; });
+        e = hipMemcpyAsync(lens_dev, hl, (size_t)p->Bt * 2 * sizeof(int32_t),
                            hipMemcpyHostToDevice, s);
         if (e != hipSuccess)
             return hip_fail(e, "sequence_lens copy");
+        e = hipEventRecord((hipEvent_t)p->lens_event, s);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipEventRecord (sequence_lens staging)");
+        p->lens_pending = 1;
+        order_dev = lens_dev + p->Bt;
     }
     InitArgs ia{};
     ia.h0 = initial_h;
@@ -251,40 +284,53 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
         return hip_fail((hipError_t)rc, "state init");
     tm.end(STAGE_OTHER);
 
-    // 3. projection of all steps, both directions in one product
-    tm.begin(STAGE_PROJ);
-    ProjArgs pr{};
-    pr.X = X;
-    pr.Wp = ws + p->ws.wp;
-    pr.XW = (float *)(ws + p->ws.xw);
-    pr.M = p->S * p->Bt;
-    pr.N = (int64_t)p->D * p->G * p->H;
-    pr.K = p->I;
-    pr.S = p->S;
-    pr.Bt = p->Bt;
-    pr.GH = (int64_t)p->G * p->H;
-    pr.layout = p->layout;
-    pr.bf16 = p->proj_bf16;
-    rc = launch_projection(pr, s);
-    if (rc)
-        return hip_fail((hipError_t)rc, "projection");
-    tm.end(STAGE_PROJ);
-
-    // 4. the step loop
-    tm.begin(STAGE_REC);
+    // 3-4. per time chunk: the projection of the chunk's steps (both
+    // directions in one launch), then its step loop
+    const int64_t nchunks = (p->S + p->C - 1) / p->C;
     RecArgs ra = rec_args(*p, ws, B, P, Y, Y_h, Y_c);
-    if (persistent) {
-        rc = launch_recurrence(ra, p->resident, 1, s);
+    for (int64_t ck = 0; ck < nchunks; ++ck) {
+        const int64_t j0 = ck * p->C, j1 = std::min<int64_t>(p->S, j0 + p->C);
+        if (ck == 0)
+            tm.begin(STAGE_PROJ);
+        ProjArgs pr{};
+        pr.X = X;
+        pr.Xb = (uint16_t *)(ws + p->ws.xb);
+        pr.Wp = ws + p->ws.wp;
+        pr.XW = (float *)(ws + p->ws.xw);
+        pr.K = p->I;
+        pr.S = p->S;
+        pr.Bt = p->Bt;
+        pr.GH = (int64_t)p->G * p->H;
+        pr.D = p->D;
+        pr.steps = p->C;
+        pr.j_base = j0;
+        pr.lens = lens_dev;
+        pr.order = order_dev;
+        pr.reverse_only = p->reverse_only;
+        pr.layout = p->layout;
+        pr.bf16 = p->proj_bf16;
+        rc = launch_projection(pr, s);
         if (rc)
-            return hip_fail((hipError_t)rc, "recurrence (persistent)");
-    } else {
-        const int32_t nq = (int32_t)(p->S * p->phases);
-        for (int32_t q = 0; q < nq; ++q) {
-            ra.q_begin = q;
-            ra.q_end = q + 1;
-            rc = launch_recurrence(ra, p->resident, 0, s);
+            return hip_fail((hipError_t)rc, "projection");
+        if (ck == 0) {
+            tm.end(STAGE_PROJ);
+            tm.begin(STAGE_REC);
+        }
+        ra.j_base = (int32_t)j0;
+        if (persistent) {
+            ra.q_begin = (int32_t)(j0 * p->phases);
+            ra.q_end = (int32_t)(j1 * p->phases);
+            rc = launch_recurrence(ra, p->resident, 1, s);
             if (rc)
-                return hip_fail((hipError_t)rc, "recurrence (per step)");
+                return hip_fail((hipError_t)rc, "recurrence (persistent)");
+        } else {
+            for (int64_t q = j0 * p->phases; q < j1 * p->phases; ++q) {
+                ra.q_begin = (int32_t)q;
+                ra.q_end = (int32_t)(q + 1);
+                rc = launch_recurrence(ra, p->resident, 0, s);
+                if (rc)
+                    return hip_fail((hipError_t)rc, "recurrence (per step)");
+            }
         }
     }
     tm.end(STAGE_REC);
@@ -429,5 +475,11 @@ extern "C" void rnn_plan_destroy(rnn_plan *p)
     for (int i = 0; i < 2 * STAGE_COUNT; ++i)
         if (p->events[i])
             (void)hipEventDestroy((hipEvent_t)p->events[i]);
+    if (p->lens_event) {
+        (void)hipEventSynchronize((hipEvent_t)p->lens_event);
+        (void)hipEventDestroy((hipEvent_t)p->lens_event);
+    }
+    if (p->lens_host)
+        (void)hipHostFree(p->lens_host);
     delete p;
 }

@@ -162,6 +162,24 @@ def test_cell_run_errors_before_any_device_work():
                            fake) == ra.RNN_ERR_INVALID_INPUT
 
 
+def test_time_chunks_shrink_the_workspace_and_lift_the_scratch_limit():
+    full = ra.RNNPlan("LSTM", 512, 64, 1024, 1024, direction="bidirectional")
+    ch = ra.RNNPlan("LSTM", 512, 64, 1024, 1024, direction="bidirectional", time_chunk=64)
+    assert "C=512" in full.describe() and "C=64" in ch.describe()
+    assert ch.workspace_bytes < full.workspace_bytes / 4
+    # a chunk at least as long as the sequence is the whole sequence
+    assert "C=20" in ra.RNNPlan("GRU", 20, 4, 8, 16, time_chunk=50).describe()
+    # 2^22 steps x 64 rows x 4 gates x 64 units exceeds 2^30 floats at once,
+    # not in chunks of 1024 steps (plan only: nothing is allocated)
+    with pytest.raises(ra.RNNError) as ei:
+        ra.RNNPlan("LSTM", 1 << 22, 64, 16, 64)
+    assert ei.value.status == ra.RNN_ERR_UNSUPPORTED
+    p = ra.RNNPlan("LSTM", 1 << 22, 64, 16, 64, time_chunk=1024)
+    assert "C=1024" in p.describe()
+    with pytest.raises(ra.RNNError):
+        ra.RNNPlan("LSTM", 8, 4, 8, 16, time_chunk=-1)
+
+
 def test_workspace_and_tiling_of_the_named_workloads():
     expect = {
         "lstm_bidir_s512_b64_i1024_h1024": dict(resident="1", workgroups="256"),
