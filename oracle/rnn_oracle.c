@@ -23,9 +23,10 @@
  * Readings where the pages are silent or garbled:
  *   - Sigmoid, Tanh, ScaledTanh, Elu and Softplus are evaluated whole in
  *     binary64 from the binary32 argument and rounded once to binary32 (the
- *     library's own polynomials are not available).  Elu uses expm1 and
- *     Softplus log1p, the accurate binary64 evaluations of exp(x)-1 and
- *     log(1+exp(x)).
+ *     library's own polynomials are not available).  The binary64 functions
+ *     follow a fixed written method (below, "Binary64 elementary functions"),
+ *     a fixed sequence of IEEE operations, so that an independent
+ *     implementation performing the same operations gets the same bits.
  *   - clip <= 0 (or NaN) clamps nothing: clip acts only when given and positive.
  *   - A wrong activation count or an unknown name is InvalidInput; surplus
  *     alpha/beta values are ignored.
@@ -89,6 +90,85 @@ static void set_err(char *err, size_t errlen, const char *msg)
 }
 
 /* ---------------------------------------------------------------------- */
+/* Binary64 elementary functions                                           */
+/* ---------------------------------------------------------------------- */
+/* The method (a reading; the pages name a polynomial document that is not
+ * available).  Every step is one IEEE binary64 operation, rounded to
+ * nearest, in the order written; no fused multiply-add.
+ *   e^x      x NaN -> x; x > 708 -> +inf; x < -708 -> +0.  Otherwise Cody and
+ *            Waite's reduction: k = rint(x * (1/ln 2)), r = (x - k*LN2_HI) -
+ *            k*LN2_LO with ln 2 = LN2_HI + LN2_LO (LN2_HI has 32 trailing zero
+ *            bits, so k*LN2_HI is exact); p = sum_{i=0..13} r^i / i! by
+ *            Horner's rule from i = 13 down; result p * 2^k.
+ *   e^x - 1  |x| < 1/2: x * (sum_{i=1..17} x^(i-1) / i!) by Horner's rule
+ *            from i = 17 down; otherwise e^x - 1.
+ *   tanh x   x NaN -> x; |x| > 22 -> copysign(1, x); otherwise
+ *            m = e^(2|x|) - 1 (as above) and copysign(m / (m + 2), x).
+ *   log(1+u) for 0 <= u <= 1: s = u / (2 + u), q = s*s,
+ *            2 * s * (sum_{n=0..20} q^n / (2n + 1)) by Horner's rule from
+ *            n = 20 down (the series of 2 atanh s).
+ * Truncation errors are below 1e-17 relative in each range. */
+static const double LN2_HI = 6.93147180369123816490e-01;   /* 0x3FE62E42FEE00000 */
+static const double LN2_LO = 1.90821492927058770002e-10;   /* 0x3DEA39EF35793C76 */
+static const double INV_LN2 = 1.44269504088896338700e+00;  /* 0x3FF71547652B82FE */
+
+static double fact_inv(int i)                 /* 1 / i!, rounded once */
+{
+    double f = 1.0;
+    for (int j = 2; j <= i; j++)
+        f = f * (double)j;                     /* exact: i! < 2^53 for i <= 18 */
+    return 1.0 / f;
+}
+
+static double orc_exp(double x)
+{
+    if (x != x)
+        return x;
+    if (x > 708.0)
+        return INFINITY;
+    if (x < -708.0)
+        return 0.0;
+    double k = rint(x * INV_LN2);
+    double r = (x - k * LN2_HI) - k * LN2_LO;
+    double p = fact_inv(13);
+    for (int i = 12; i >= 0; i--)
+        p = p * r + fact_inv(i);
+    return ldexp(p, (int)k);
+}
+
+static double orc_expm1(double x)
+{
+    if (fabs(x) < 0.5) {
+        double p = fact_inv(17);
+        for (int i = 16; i >= 1; i--)
+            p = p * x + fact_inv(i);
+        return x * p;
+    }
+    return orc_exp(x) - 1.0;
+}
+
+static double orc_tanh(double x)
+{
+    if (x != x)
+        return x;
+    double ax = fabs(x);
+    if (ax > 22.0)
+        return copysign(1.0, x);
+    double m = orc_expm1(2.0 * ax);
+    return copysign(m / (m + 2.0), x);
+}
+
+static double orc_log1p01(double u)            /* 0 <= u <= 1 */
+{
+    double s = u / (2.0 + u);
+    double q = s * s;
+    double p = 1.0 / 41.0;
+    for (int n = 19; n >= 0; n--)
+        p = p * q + 1.0 / (double)(2 * n + 1);
+    return 2.0 * s * p;
+}
+
+/* ---------------------------------------------------------------------- */
 /* Activations ("Activations", definitions paragraph)                      */
 /* ---------------------------------------------------------------------- */
 
@@ -96,9 +176,9 @@ float orc_activation(int32_t kind, float alpha, float beta, float x)
 {
     switch (kind) {
     case ACT_SIGMOID:
-        return (float)(1.0 / (1.0 + exp(-(double)x)));
+        return (float)(1.0 / (1.0 + orc_exp(-(double)x)));
     case ACT_TANH:
-        return (float)tanh((double)x);
+        return (float)orc_tanh((double)x);
     case ACT_RELU:                       /* keeps a NaN (and -0) */
         return x < 0.0f ? 0.0f : x;
     case ACT_AFFINE: {
@@ -110,7 +190,7 @@ float orc_activation(int32_t kind, float alpha, float beta, float x)
     case ACT_THRESHOLDEDRELU:
         return x > alpha ? x : 0.0f;
     case ACT_SCALEDTANH:
-        return (float)((double)alpha * tanh((double)beta * (double)x));
+        return (float)((double)alpha * orc_tanh((double)beta * (double)x));
     case ACT_HARDSIGMOID: {
         float ax = alpha * x;
         float y = ax + beta;
@@ -119,13 +199,17 @@ float orc_activation(int32_t kind, float alpha, float beta, float x)
         return y;
     }
     case ACT_ELU:
-        return x >= 0.0f ? x : (float)((double)alpha * expm1((double)x));
+        return x >= 0.0f ? x : (float)((double)alpha * orc_expm1((double)x));
     case ACT_SOFTSIGN: {
         float den = 1.0f + fabsf(x);
         return x / den;
     }
     case ACT_SOFTPLUS:
-        return x > 20.0f ? x : (float)log1p(exp((double)x));
+        if (x > 20.0f)                  /* log(1 + e^x) rounds to x */
+            return x;
+        if (x > 0.0f)                   /* x + log(1 + e^-x) */
+            return (float)((double)x + orc_log1p01(orc_exp(-(double)x)));
+        return (float)orc_log1p01(orc_exp((double)x));   /* NaN passes through */
     default:
         return NAN;
     }
