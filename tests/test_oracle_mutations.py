@@ -29,7 +29,12 @@ MUTATIONS = {
     "hardsigmoid_default_beta": ("case ACT_HARDSIGMOID: return 0.5f;", "case ACT_HARDSIGMOID: return 0.0f;"),
     "gemm_k_descending": ("for (int64_t k = 0; k < K; k++) {", "for (int64_t k = K - 1; k >= 0; k--) {"),
     "y_not_zeroed_past_len": ("Y[i] = 0.0f;            /* positions", "(void)0;            /* positions"),
-    "sigmoid_sign": ("1.0 / (1.0 + exp(-(double)x))", "1.0 / (1.0 + exp((double)x))"),
+    "sigmoid_sign": ("1.0 / (1.0 + orc_exp(-(double)x))", "1.0 / (1.0 + orc_exp((double)x))"),
+    "exp_poly_drops_constant_term": ("for (int i = 12; i >= 0; i--)", "for (int i = 12; i >= 1; i--)"),
+    "exp_reduction_drops_ln2_tail": ("double r = (x - k * LN2_HI) - k * LN2_LO;",
+                                     "double r = (x - k * LN2_HI);"),
+    "tanh_wrong_denominator": ("copysign(m / (m + 2.0), x)", "copysign(m / (m + 1.0), x)"),
+    "log1p_series_too_short": ("for (int n = 19; n >= 0; n--)", "for (int n = 2; n >= 0; n--)"),
     "layout1_state_index": ("(size_t)((b * D + d) * H)", "(size_t)((d * Bt + b) * H)"),
     "input_forget_uses_i": ("? 1.0f - ig", "? ig"),
     "no_nan_canonicalisation": ("if (v != v) {", "if (0) {"),
@@ -61,6 +66,7 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     env = dict(os.environ, RNN_ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_invariants.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_invariants.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_elementary.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"planted mistake {name} was not caught:\n{r.stdout[-2000:]}"
