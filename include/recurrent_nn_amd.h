@@ -115,6 +115,14 @@ typedef struct rnn_attrs {
                                           chunks, so the scratch limit applies to the chunk
                                           length instead of seq_length.  Results are
                                           identical either way.                          */
+    int32_t exact;                     /* 1 = exact mode (onemodel "Exact mode"): every
+                                          product value is one binary32 accumulator over
+                                          k in increasing order from +0, each multiply and
+                                          add rounded on its own (no matrix cores), and
+                                          the transcendental activations follow one fixed
+                                          binary64 method; results do not depend on the
+                                          tiling and match that definition bit for bit.
+                                          0 = fast mode (matrix-core products).           */
 } rnn_attrs;
 
 /* Dimensions: hidden is R's last dimension, num_directions W's first. */

@@ -111,7 +111,8 @@ def make_attrs(op: str, direction: str = "forward", hidden_size: int = 0, layout
                input_forget: int = 0, linear_before_reset: int = 0, proj_bf16: bool = False,
                constant_weights: bool = False, kernel_path: int = RNN_PATH_AUTO,
                units_per_block: int = 0, batch_tile: int = 0, waves_per_block: int = 0,
-               barrier_spin_limit: int = 0, batch_halves: int = 0, time_chunk: int = 0):
+               barrier_spin_limit: int = 0, batch_halves: int = 0, time_chunk: int = 0,
+               exact: bool = False):
     """Returns (attrs, keepalive); keep `keepalive` alive while attrs is used."""
     keep = []
     a = rnn_attrs()
@@ -148,6 +149,7 @@ def make_attrs(op: str, direction: str = "forward", hidden_size: int = 0, layout
     a.barrier_spin_limit = barrier_spin_limit
     a.batch_halves = batch_halves
     a.time_chunk = time_chunk
+    a.exact = 1 if exact else 0
     return a, keep
 
 

@@ -51,6 +51,7 @@ class rnn_attrs(ctypes.Structure):
         ("barrier_spin_limit", ctypes.c_int32),
         ("batch_halves", ctypes.c_int32),
         ("time_chunk", ctypes.c_int32),
+        ("exact", ctypes.c_int32),
     ]
 
 

@@ -86,6 +86,7 @@ struct rnn_plan {
     int32_t KB = 1;           // 16-wide k blocks per wave (Hp / (16 * NW))
     int32_t resident = 0;     // R slice held in registers across steps
     int32_t halves = 1;       // 2: each step as two half-batch sub-steps (rec_pipe_kernel)
+    int32_t exact = 0;        // exact mode: k-ordered unfused products, exact activations
     int64_t Btp = 16;         // NBB * BT
     int32_t n_wg = 1;         // D * NBB * NUB
 
@@ -162,6 +163,7 @@ struct ProjArgs {
     int32_t reverse_only;   // direction 0 runs in reverse
     int32_t layout;         // 0: X [S][Bt][I]; 1: X [Bt][S][I]
     int32_t bf16;
+    int32_t exact;          // exact mode: one accumulator per output, k in order, VALU
 };
 int launch_projection(const ProjArgs &a, void *stream);
 
@@ -171,6 +173,7 @@ struct RecArgs {
     int32_t Hp, KB, NW, U, NUB, BT, NBB, MT, NTA, NTB, NT, phases;
     int32_t Btp;
     int32_t halves;         // 1, or 2 half-batch sub-steps per step (rec_pipe_kernel)
+    int32_t exact;          // exact mode (rec_exact_kernel)
     int32_t reverse_only, layout, clip_on, input_forget, lbr;
     float clip;
     ActSpec act[2][3];

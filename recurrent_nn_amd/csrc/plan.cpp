@@ -270,6 +270,17 @@ rnn_status choose_tiling(const rnn_attrs &a, rnn_plan &p)
         return RNN_ERR_INVALID_INPUT;
     }
     p.halves = (halves_ok && a.batch_halves != 1) ? 2 : 1;
+    if (p.exact) {
+        p.halves = 1;                              // the exact kernel has one form
+        if (a.batch_halves == 2) {
+            set_error("batch_halves = 2 is a fast-mode schedule; exact mode has one form");
+            return RNN_ERR_INVALID_INPUT;
+        }
+        if (p.NT * 16 > 128) {
+            set_error("exact mode supports at most 128 gate columns per workgroup");
+            return RNN_ERR_UNSUPPORTED;
+        }
+    }
     return RNN_OK;
 }
 
@@ -373,6 +384,9 @@ extern "C" rnn_status rnn_plan_create(const rnn_attrs *attrs, const rnn_dims *di
     p->kernel_path = a.kernel_path;
     if (a.time_chunk < 0)
         return fail(RNN_ERR_INVALID_INPUT, "time_chunk must be >= 0");
+    if (a.exact != 0 && a.exact != 1)
+        return fail(RNN_ERR_INVALID_INPUT, "exact must be 0 or 1");
+    p->exact = a.exact;
     p->C = (a.time_chunk > 0 && a.time_chunk < p->S) ? a.time_chunk : p->S;
     if (a.barrier_spin_limit < 0)
         return fail(RNN_ERR_INVALID_INPUT, "barrier_spin_limit must be >= 0");
@@ -430,11 +444,11 @@ extern "C" rnn_status rnn_plan_describe(const rnn_plan *p, char *buf, size_t len
     std::snprintf(buf, len,
                   "op=%d G=%d D=%d S=%lld C=%lld Bt=%lld I=%lld H=%lld U=%d NUB=%d BT=%d NBB=%d "
                   "MT=%d NTA=%d NTB=%d phases=%d Hp=%lld waves=%d KB=%d resident=%d halves=%d "
-                  "workgroups=%d path=%d persist=%d ws=%zu",
+                  "exact=%d workgroups=%d path=%d persist=%d ws=%zu",
                   p->op, p->G, p->D, (long long)p->S, (long long)p->C, (long long)p->Bt,
                   (long long)p->I,
                   (long long)p->H, p->U, p->NUB, p->BT, p->NBB, p->MT, p->NTA, p->NTB, p->phases,
-                  (long long)p->Hp, p->NW, p->KB, p->resident, p->halves, p->n_wg, p->kernel_path,
+                  (long long)p->Hp, p->NW, p->KB, p->resident, p->halves, p->exact, p->n_wg, p->kernel_path,
                   p->can_persist, p->ws.total);
     return RNN_OK;
 }

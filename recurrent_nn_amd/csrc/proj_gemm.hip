@@ -298,10 +298,121 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs a)
         }
 }
 
+// Exact mode (onemodel "Recurrent operators", section "Exact mode"): each
+// XW value is one accumulator that starts at +0 and adds the binary32
+// products X[m][k] * W[n][k] for k = 0, 1, ..., K-1 in order, every multiply
+// and add rounded on its own (for bf16 the operands are the rounded bf16
+// values, whose products are exact in binary32).  VALU only; the value does
+// not depend on the tiling.  64x64 tile per 256-thread workgroup, each
+// thread 4x4 outputs (rows ty + 16 i, columns tx + 16 j), k staged through
+// LDS in chunks of 32.  Same rows, tile skip and XW order as the fast form.
+template <bool BF16>
+__global__ void __launch_bounds__(256) proj_exact_kernel(ProjArgs a)
+{
+    constexpr int TM = 64, TN = 64, KC = 32;
+    __shared__ float As[KC][TM + 1], Bs[KC][TN + 1];
+    __shared__ int64_t xrow_s[TM];
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int64_t Md = a.steps * a.Bt;
+    const int64_t tiles_m = (Md + TM - 1) / TM, tiles_n = (a.GH + TN - 1) / TN;
+    const int64_t tmg = blockIdx.x / tiles_n, tn = blockIdx.x - tmg * tiles_n;
+    const int64_t d = tmg / tiles_m, tm = tmg - d * tiles_m;
+    const int64_t m0 = tm * TM, n0 = tn * TN;
+    int any = 0;
+    if (tid < TM) {
+        xrow_s[tid] = proj_xrow(a, d, m0 + tid);
+        any = xrow_s[tid] >= 0;
+    }
+    if (!__syncthreads_or(any))
+        return;                                      // no row of this tile is ever read
+    const float *X = (const float *)a.X;
+    const uint16_t *Xb = BF16 ? a.Xb + (size_t)d * Md * a.K : nullptr;
+    const char *Wd = (const char *)a.Wp + (size_t)d * a.GH * a.K * (BF16 ? 2 : 4);
+    auto bf = [](uint16_t h) { return __uint_as_float((uint32_t)h << 16); };
+
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = 0.0f;
+    for (int64_t k0 = 0; k0 < a.K; k0 += KC) {
+        const int kn = (int)(a.K - k0 < KC ? a.K - k0 : KC);
+        for (int e = tid; e < TM * KC; e += 256) {
+            const int r = e / KC, kk = e - r * KC;
+            const int64_t k = k0 + kk;
+            float va = 0.0f, vb = 0.0f;
+            if (kk < kn) {
+                if (BF16) {
+                    if (m0 + r < Md)
+                        va = bf(Xb[(size_t)(m0 + r) * a.K + k]);
+                    if (n0 + r < a.GH)
+                        vb = bf(((const uint16_t *)Wd)[(size_t)(n0 + r) * a.K + k]);
+                } else {
+                    if (xrow_s[r] >= 0)
+                        va = X[(size_t)xrow_s[r] * a.K + k];
+                    if (n0 + r < a.GH)
+                        vb = ((const float *)Wd)[(size_t)(n0 + r) * a.K + k];
+                }
+            }
+            As[kk][r] = va;
+            Bs[kk][r] = vb;
+        }
+        __syncthreads();
+        for (int kk = 0; kk < kn; ++kk) {
+            float av[4], bv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                av[i] = As[kk][ty + 16 * i];
+                bv[i] = Bs[kk][tx + 16 * i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __fadd_rn(acc[i][j], __fmul_rn(av[i], bv[j]));
+        }
+        __syncthreads();
+    }
+    float *XWd = a.XW + (size_t)d * Md * a.GH;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + ty + 16 * i;
+        if (m >= Md)
+            continue;
+        const uint32_t jl = (uint32_t)m / (uint32_t)a.Bt, ii = (uint32_t)m - jl * (uint32_t)a.Bt;
+        const size_t b = a.order ? (size_t)a.order[ii] : ii;
+        const size_t ro = ((size_t)jl * a.Bt + b) * a.GH;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t n = n0 + tx + 16 * j;
+            if (n < a.GH)
+                XWd[ro + n] = acc[i][j];
+        }
+    }
+}
+
 int launch_projection(const ProjArgs &a, void *stream)
 {
     if (a.steps <= 0 || a.Bt <= 0 || a.GH <= 0)
         return 0;
+    if (a.exact) {
+        if (a.bf16) {
+            int64_t blocks = a.D * a.steps * a.Bt;
+            if (blocks > 65536)
+                blocks = 65536;
+            hipLaunchKernelGGL(gather_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                               (hipStream_t)stream, a);
+        }
+        const int64_t et = a.D * ((a.steps * a.Bt + 63) / 64) * ((a.GH + 63) / 64);
+        if (a.bf16)
+            hipLaunchKernelGGL(proj_exact_kernel<true>, dim3((unsigned)et), dim3(256), 0,
+                               (hipStream_t)stream, a);
+        else
+            hipLaunchKernelGGL(proj_exact_kernel<false>, dim3((unsigned)et), dim3(256), 0,
+                               (hipStream_t)stream, a);
+        return (int)hipGetLastError();
+    }
     const int64_t tiles = a.D * ((a.steps * a.Bt + BM - 1) / BM) * ((a.GH + BN - 1) / BN);
     const size_t shmem = 2 * 2 * TILEB;
     const void *fn = a.bf16 ? (const void *)proj_gemm_kernel<true> : (const void *)proj_gemm_kernel<false>;

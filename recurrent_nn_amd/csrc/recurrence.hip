@@ -3,6 +3,7 @@
 // persistent (cooperative) form, and the launches.
 #include <hip/hip_runtime.h>
 
+#include "recurrence_exact.h"
 #include "recurrence_pipe.h"
 
 namespace rnnamd {
@@ -77,6 +78,8 @@ static rec_fn get_pipe(int act, int mth, int nt, int kb)
 
 static rec_fn pick(const RecArgs &a, int resident)
 {
+    if (a.exact)    // exact mode: one kernel for every shape (up to 128 columns per block)
+        return a.NT * 16 <= 128 ? rec_exact_kernel : nullptr;
     if (a.halves == 2) {
         // two half-batch sub-steps per step: R in registers, four waves, one
         // phase, at most two pairs per thread and half
@@ -117,10 +120,12 @@ bool recurrence_supported(int nw, int mt, int nt, int nta, int phases, int kb, i
 
 static size_t rec_shmem(const RecArgs &a)
 {
+    if (a.exact)
+        return rec_exact_lds_bytes(a.BT, a.NT, a.U);
     return a.halves == 2 ? rec_pipe_lds_bytes(a.BT, a.NT, a.U) : rec_lds_bytes(a.NW, a.BT, a.NT, a.U);
 }
 
-static int rec_threads(const RecArgs &a) { return 64 * a.NW; }
+static int rec_threads(const RecArgs &a) { return a.exact ? 256 : 64 * a.NW; }
 
 int recurrence_can_persist(const RecArgs &a, int resident, int device, int *ok)
 {

@@ -254,6 +254,41 @@ __device__ __forceinline__ float gates_one_phase(int op, const float *xv, Rec re
     return og * hc;
 }
 
+// GRU with linear_before_reset = 0, in the written order.  First phase: the
+// update and reset gates from their XW values and recurrent products;
+// returns z and stores r in *r.  Second phase: the candidate from its XW
+// value and the product over r (.) H_prev, then the new h.
+template <typename F>
+__device__ __forceinline__ float gru0_gates(float xz, float xr, float rz, float rr, const float *cu,
+                                            int U, int u, bool clip_on, float clip, F f, float *r)
+{
+    float pz = xz + rz;
+    float pr = xr + rr;
+    pz = pz + cu[u];
+    pz = pz + cu[4 * U + u];
+    pr = pr + cu[U + u];
+    pr = pr + cu[5 * U + u];
+    pz = clip_pre(pz, clip_on, clip);
+    pr = clip_pre(pr, clip_on, clip);
+    *r = f(pr);
+    return f(pz);
+}
+
+template <typename Gf>
+__device__ __forceinline__ float gru0_candidate(float xh, float rh, const float *cu, int U, int u,
+                                                bool clip_on, float clip, float z, float hp, Gf g)
+{
+    float ph = xh + rh;
+    ph = ph + cu[2 * U + u];
+    ph = ph + cu[6 * U + u];
+    ph = clip_pre(ph, clip_on, clip);
+    const float ht = g(ph);
+    const float omz = 1.0f - z;
+    const float a1 = omz * ht;
+    const float a2 = z * hp;
+    return a1 + a2;
+}
+
 // LDS bytes of one workgroup: the four partial tiles, then the per-pair
 // states (h, c, z) and the per-row lengths.
 __host__ __device__ inline size_t rec_lds_bytes(int nw, int bt, int nt, int u)
@@ -498,28 +533,13 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
                         op, xv, [&](int g) { return rec_at(rl, g * uc + u); }, cst_u, a.U, u,
                         Pd != nullptr, a.clip_on, a.clip, a.input_forget != 0, hp, cn, F, Gf, Hf);
                 } else if (ph == 0) {                       // GRU lbr = 0: z and r
-                    float pz = xv[0] + rec_at(rl, u);
-                    float pr = xv[1] + rec_at(rl, uc + u);
-                    pz = pz + cst_u[u];
-                    pz = pz + cst_u[4 * a.U + u];
-                    pr = pr + cst_u[a.U + u];
-                    pr = pr + cst_u[5 * a.U + u];
-                    pz = clip_pre(pz, a.clip_on, a.clip);
-                    pr = clip_pre(pr, a.clip_on, a.clip);
-                    zst[pi] = F(pz);
-                    const float r = F(pr);
+                    float r;
+                    zst[pi] = gru0_gates(xv[0], xv[1], rec_at(rl, u), rec_at(rl, uc + u), cst_u,
+                                         a.U, u, a.clip_on, a.clip, F, &r);
                     store_coherent(snext + (size_t)rl * Hp + gu, r * hp);   // r (.) H_prev
                 } else {                                    // GRU lbr = 0: candidate
-                    float ph_ = xv[2] + rec_at(rl, a.NTA * 16 + u);
-                    ph_ = ph_ + cst_u[2 * a.U + u];
-                    ph_ = ph_ + cst_u[6 * a.U + u];
-                    ph_ = clip_pre(ph_, a.clip_on, a.clip);
-                    const float ht = Gf(ph_);
-                    const float z = zst[pi];
-                    const float omz = 1.0f - z;
-                    const float a1 = omz * ht;
-                    const float a2 = z * hp;
-                    hn = a1 + a2;
+                    hn = gru0_candidate(xv[2], rec_at(rl, a.NTA * 16 + u), cst_u, a.U, u,
+                                        a.clip_on, a.clip, zst[pi], hp, Gf);
                 }
             } else if (a.phases == 2 && ph == 0) {
                 store_coherent(snext + (size_t)rl * Hp + gu, 0.0f);

@@ -66,6 +66,7 @@ RecArgs rec_args(const rnn_plan &p, unsigned char *ws, const float *B, const flo
     r.phases = p.phases;
     r.Btp = (int32_t)p.Btp;
     r.halves = p.halves;
+    r.exact = p.exact;
     r.reverse_only = p.reverse_only;
     r.layout = p.layout;
     r.clip_on = p.clip_on;
@@ -309,6 +310,7 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
         pr.reverse_only = p->reverse_only;
         pr.layout = p->layout;
         pr.bf16 = p->proj_bf16;
+        pr.exact = p->exact;
         rc = launch_projection(pr, s);
         if (rc)
             return hip_fail((hipError_t)rc, "projection");
