@@ -27,6 +27,11 @@ sys.path.insert(0, ROOT)
 METRIC = "LSTM/GRU cell-updates/s (seq·batch·dirs per s) + % of HBM/MFMA roofline, 1 GPU"
 FP32_MFMA_PEAK_TFLOPS = 157.3      # MI355X dense fp32 matrix peak
 BF16_MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+# Exact mode's roof: binary32 multiplies and adds issued separately on the
+# vector ALUs.  The published fp32 vector peak (157.3 TFLOP/s = 256 CUs x 4
+# SIMDs x 32 lanes x 2 flops x 2.4 GHz) counts a fused multiply-add as two
+# flops; with the multiply and the add as two instructions it is half.
+FP32_VALU_MULADD_PEAK_TFLOPS = 157.3 / 2
 HBM_PEAK_GBS = 8000.0
 
 
@@ -39,6 +44,10 @@ def parse():
     p.add_argument("--kernel-path", type=int, default=0, help="0 auto, 1 persistent, 2 per step")
     p.add_argument("--cpu-budget-s", type=float, default=30.0, help="0 skips the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--exact", action="store_true",
+                   help="exact mode: k-ordered unfused products on the VALU (results bit-identical "
+                        "to the oracle); reported against the fp32 vector peak")
+    p.add_argument("--time-chunk", type=int, default=0, help="steps per time chunk (0: all)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB -> 1 GiB device copy kernel (to scale HBM counters)")
     p.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -231,7 +240,8 @@ def main():
     print(f"[bench] workload {c.name}: inputs drawn", file=sys.stderr, flush=True)
     t = {k: (v.to(dev) if v is not None and k != "sequence_lens" else v)
          for k, v in c.tensors().items()}
-    plan = ra.plan_for_case(c, kernel_path=args.kernel_path)
+    plan = ra.plan_for_case(c, kernel_path=args.kernel_path, exact=args.exact,
+                            time_chunk=args.time_chunk)
     Y = torch.empty(plan.output_shapes()[0], dtype=torch.float32, device=dev)
     Yh = torch.empty(plan.output_shapes()[1], dtype=torch.float32, device=dev)
     Yc = torch.empty_like(Yh) if c.op == "LSTM" else None
@@ -277,13 +287,19 @@ def main():
 
     proj_f, rec_f = flops_per_run(c)
     proj_peak = BF16_MFMA_PEAK_TFLOPS if c.proj_bf16 else FP32_MFMA_PEAK_TFLOPS
+    bound = "mfma"
+    if args.exact:
+        proj_peak = rec_peak = FP32_VALU_MULADD_PEAK_TFLOPS
+        bound = "alu"
+    else:
+        rec_peak = FP32_MFMA_PEAK_TFLOPS
     kernels = {
-        "projection": {"bound": "mfma", "flop": proj_f, "ms": stage_ms["projection"],
+        "projection": {"bound": bound, "flop": proj_f, "ms": stage_ms["projection"],
                        "achieved": proj_f / (stage_ms["projection"] * 1e-3) / 1e12,
                        "peak": proj_peak, "unit": "TFLOP/s"},
-        "recurrence": {"bound": "mfma", "flop": rec_f, "ms": stage_ms["recurrence"],
+        "recurrence": {"bound": bound, "flop": rec_f, "ms": stage_ms["recurrence"],
                        "achieved": rec_f / (stage_ms["recurrence"] * 1e-3) / 1e12,
-                       "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "peak": rec_peak, "unit": "TFLOP/s",
                        "us_per_step": stage_ms["recurrence"] * 1e3 / c.seq},
     }
     for k in kernels.values():
@@ -302,7 +318,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16+f32" if c.proj_bf16 else "f32",
         "data": "synthetic",
-        "config": {"workload": c.name, "op": c.op, "direction": c.direction, "seq": c.seq,
+        "config": {"workload": c.name, "mode": "exact" if args.exact else "fast",
+                   "time_chunk": args.time_chunk, "op": c.op, "direction": c.direction, "seq": c.seq,
                    "batch": c.batch, "input": c.input, "hidden": c.hidden, "dirs": c.dirs,
                    "layout": c.layout, "global_batch": c.batch, "seq_len": c.seq,
                    "parallelism": "none (1 GPU)", "plan": plan.describe()},
