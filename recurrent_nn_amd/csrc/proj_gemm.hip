@@ -14,8 +14,10 @@
 // launch (the direction is part of the tile index).
 //
 // Tiling: 128x128 output tile per 256-thread workgroup, 4 waves of 64x64, K
-// staged through LDS in 128-byte row slices (32 fp32 or 64 bf16 values) with
-// double buffering.  fp32 uses v_mfma_f32_16x16x4_f32, bf16 uses the gfx950
+// staged through LDS in 128-byte row slices (32 fp32 or 64 bf16 values): the
+// next slice is loaded into registers while the current one is consumed and
+// replaces it between two barriers, so one LDS buffer (36 KiB) suffices and
+// three workgroups share a CU (measured faster than two double-buffered).  fp32 uses v_mfma_f32_16x16x4_f32, bf16 uses the gfx950
 // v_mfma_f32_16x16x32_bf16; for bf16, the chunk's X rows are first gathered
 // and rounded to bfloat16 (nearest even) once by gather_bf16_kernel.  Accumulation is in the
 // matrix cores' order with a fixed tiling (deterministic, "fast mode").
@@ -162,9 +164,9 @@ __device__ __forceinline__ void tile_of(int64_t wg, int64_t nwg, int64_t tiles_m
 }
 
 template <bool BF16>
-__global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs a)
+__global__ void __launch_bounds__(256, 3) proj_gemm_kernel(ProjArgs a)
 {
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];   // [2][A,B][TILEB]
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];   // [A,B][TILEB]
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lq = lane >> 4;
@@ -263,17 +265,20 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs a)
                 }
         }
     };
+    // one LDS buffer: the next stage waits in registers while this one is
+    // consumed, then replaces it between two barriers
     gload(0, ra, rb);
     sstore(0, ra, rb);
     __syncthreads();
     for (int64_t kt = 0; kt < nk; ++kt) {
-        const int buf = (int)(kt & 1);
         if (kt + 1 < nk)
             gload(kt + 1, ra, rb);
-        stage(buf);
-        if (kt + 1 < nk)
-            sstore(buf ^ 1, ra, rb);
+        stage(0);
         __syncthreads();
+        if (kt + 1 < nk) {
+            sstore(0, ra, rb);
+            __syncthreads();
+        }
     }
 
     // store: lane holds rows 4*lq + r, column lr of each 16x16 tile; logical
@@ -414,7 +419,7 @@ int launch_projection(const ProjArgs &a, void *stream)
         return (int)hipGetLastError();
     }
     const int64_t tiles = a.D * ((a.steps * a.Bt + BM - 1) / BM) * ((a.GH + BN - 1) / BN);
-    const size_t shmem = 2 * 2 * TILEB;
+    const size_t shmem = 2 * TILEB;               // one buffer of A and B
     const void *fn = a.bf16 ? (const void *)proj_gemm_kernel<true> : (const void *)proj_gemm_kernel<false>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess)

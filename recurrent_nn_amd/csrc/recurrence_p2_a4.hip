@@ -6,12 +6,13 @@
 namespace rnnamd {
 
 // mth 16-row tiles per half (BT = 32 * mth), nt 16-column tiles, kb 16-k
-// blocks per wave (R slice of nt * kb * 4 registers per lane).
-rec_fn rec_get_pipe_a4(int mth, int nt, int kb)
+// blocks per wave (R slice of nt * kb * 4 registers per lane), p pairs per
+// thread and half (1 or 2).
+rec_fn rec_get_pipe_a4(int mth, int nt, int kb, int p)
 {
 #define RNN_P2(MTH_, NT_, KB_)                                                                    \
     if (mth == MTH_ && nt == NT_ && kb == KB_)                                                   \
-        return rec_pipe_kernel<MTH_, NT_, KB_, 4>;
+        return p == 1 ? rec_pipe_kernel<MTH_, NT_, KB_, 4, 1> : rec_pipe_kernel<MTH_, NT_, KB_, 4, 2>;
     RNN_P2(1, 1, 8)
     RNN_P2(1, 1, 16)
     RNN_P2(1, 2, 8)

@@ -120,14 +120,14 @@ __host__ __device__ inline size_t rec_pipe_lds_bytes(int bt, int nt, int u)
 // block than the full tile, so more blocks in flight; 3 measured best).
 constexpr int kPipePrefetch = 3;
 
-template <int MTH, int NT, int KBR, int ACT>
+template <int MTH, int NT, int KBR, int ACT, int P>
 __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
 {
     constexpr int BTH = MTH * 16;                // rows per half
     constexpr int BT = 2 * BTH;
     constexpr int NTC = NT * 16;
     constexpr int LDR = NTC + 4;
-    constexpr int P = 2;                         // pairs per thread and half, at most
+    // P: pairs per thread and half, at most (1 or 2)
     constexpr int KH = KBR / 2;                  // k block where the other half is published
     // k block where the next product's flags are polled: after the publish
     // and after the last A prefetch is issued
