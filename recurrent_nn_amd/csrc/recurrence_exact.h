@@ -189,7 +189,8 @@ __global__ void __launch_bounds__(256, 1) rec_exact_kernel(RecArgs a)
             if (active) {
                 if (a.phases == 1) {
                     hn = gates_one_phase(
-                        op, xv, [&](int g) { return rr[g * uc + u]; }, cst_u, a.U, u, Pd != nullptr,
+                        op, xv, [&](int g) { return rr[g * uc + u]; },
+                        [&](int e) { return cst_u[e * a.U + u]; }, Pd != nullptr,
                         a.clip_on, a.clip, a.input_forget != 0, hp, cn, F, Gf, Hf);
                 } else if (ph == 0) {                   // GRU lbr = 0: z and r
                     float r;

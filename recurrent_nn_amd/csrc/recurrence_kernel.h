@@ -179,38 +179,39 @@ __device__ __forceinline__ void product_stream(f4 (&acc)[MT][NT], const float *a
 
 // Gate arithmetic of one (row, unit) pair for the single-phase operators (RNN,
 // GRU with linear_before_reset = 1, LSTM), in the written order.  xv[g] is the
-// pair's XW value of gate g, rec(g) its recurrent product, cu the staged
-// per-unit constants ([11][U]: Wb and Rb per gate, then Pi, Po, Pf), hp the
-// previous h and c the LSTM cell state (updated in place).  Returns the new h.
-template <typename F, typename Gf, typename Hf, typename Rec>
-__device__ __forceinline__ float gates_one_phase(int op, const float *xv, Rec rec, const float *cu,
-                                                 int U, int u, bool peep, bool clip_on, float clip,
+// pair's XW value of gate g, rec(g) its recurrent product, cst(e) the pair's
+// per-unit constants (e = g: Wb of gate g, 4 + g: Rb of gate g, 8, 9, 10: Pi,
+// Po, Pf), hp the previous h and c the LSTM cell state (updated in place).
+// Returns the new h.
+template <typename F, typename Gf, typename Hf, typename Rec, typename Cst>
+__device__ __forceinline__ float gates_one_phase(int op, const float *xv, Rec rec, Cst cst,
+                                                 bool peep, bool clip_on, float clip,
                                                  bool input_forget, float hp, float &c, F f, Gf g,
                                                  Hf h)
 {
     if (op == RNN_OP_RNN) {
         float pre = xv[0] + rec(0);
-        pre = pre + cu[u];
-        pre = pre + cu[4 * U + u];
+        pre = pre + cst(0);
+        pre = pre + cst(4);
         pre = clip_pre(pre, clip_on, clip);
         return f(pre);
     }
     if (op == RNN_OP_GRU) {                                 // linear_before_reset = 1
         float pz = xv[0] + rec(0);
         float pr = xv[1] + rec(1);
-        pz = pz + cu[u];
-        pz = pz + cu[4 * U + u];
-        pr = pr + cu[U + u];
-        pr = pr + cu[5 * U + u];
+        pz = pz + cst(0);
+        pz = pz + cst(4);
+        pr = pr + cst(1);
+        pr = pr + cst(5);
         pz = clip_pre(pz, clip_on, clip);
         pr = clip_pre(pr, clip_on, clip);
         const float z = f(pz);
         const float r = f(pr);
         float rh = rec(2);
-        rh = rh + cu[6 * U + u];
+        rh = rh + cst(6);
         const float gated = r * rh;
         float ph = xv[2] + gated;
-        ph = ph + cu[2 * U + u];
+        ph = ph + cst(2);
         ph = clip_pre(ph, clip_on, clip);
         const float ht = g(ph);
         const float omz = 1.0f - z;
@@ -223,14 +224,14 @@ __device__ __forceinline__ float gates_one_phase(int op, const float *xv, Rec re
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         float v = xv[k] + rec(k);
-        v = v + cu[k * U + u];
-        v = v + cu[(4 + k) * U + u];
+        v = v + cst(k);
+        v = v + cst(4 + k);
         pre[k] = v;
     }
     const float cp = c;
     if (peep) {
-        const float pi_ = cu[8 * U + u] * cp;
-        const float pf_ = cu[10 * U + u] * cp;
+        const float pi_ = cst(8) * cp;
+        const float pf_ = cst(10) * cp;
         pre[0] = pre[0] + pi_;
         pre[2] = pre[2] + pf_;
     }
@@ -245,7 +246,7 @@ __device__ __forceinline__ float gates_one_phase(int op, const float *xv, Rec re
     c = k1 + k2;
     float po = pre[1];
     if (peep) {
-        const float pov = cu[9 * U + u] * c;
+        const float pov = cst(9) * c;
         po = po + pov;
     }
     po = clip_pre(po, clip_on, clip);
@@ -530,8 +531,8 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
             if (active) {
                 if (op != RNN_OP_GRU || a.phases == 1) {    // (compile-time for LSTM, RNN)
                     hn = gates_one_phase(
-                        op, xv, [&](int g) { return rec_at(rl, g * uc + u); }, cst_u, a.U, u,
-                        Pd != nullptr, a.clip_on, a.clip, a.input_forget != 0, hp, cn, F, Gf, Hf);
+                        op, xv, [&](int g) { return rec_at(rl, g * uc + u); },
+                        [&](int e) { return cst_u[e * a.U + u]; }, Pd != nullptr, a.clip_on, a.clip, a.input_forget != 0, hp, cn, F, Gf, Hf);
                 } else if (ph == 0) {                       // GRU lbr = 0: z and r
                     float r;
                     zst[pi] = gru0_gates(xv[0], xv[1], rec_at(rl, u), rec_at(rl, uc + u), cst_u,

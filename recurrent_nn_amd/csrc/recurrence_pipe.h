@@ -109,11 +109,12 @@ __device__ __forceinline__ void product_res_hooked(f4 (&acc)[MT][NT],
     }
 }
 
-// LDS bytes: partial tiles of both halves, h and c per pair, lengths, the
-// per-unit constants, two publish counters.
+// LDS bytes: partial tiles of both halves (column-major, BT/2 + 4 rows per
+// column), h and c per pair, lengths, the per-unit constants, two publish
+// counters.
 __host__ __device__ inline size_t rec_pipe_lds_bytes(int bt, int nt, int u)
 {
-    return ((size_t)4 * bt * (nt * 16 + 4) + 2 * (size_t)bt * u + bt + 11 * (size_t)u + 2) * 4;
+    return ((size_t)8 * nt * 16 * (bt / 2 + 4) + 2 * (size_t)bt * u + bt + 11 * (size_t)u + 2) * 4;
 }
 
 // Depth of the A prefetch for the half-height products (fewer MFMAs per k
@@ -126,7 +127,9 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
     constexpr int BTH = MTH * 16;                // rows per half
     constexpr int BT = 2 * BTH;
     constexpr int NTC = NT * 16;
-    constexpr int LDR = NTC + 4;
+    constexpr int LDC = BTH + 4;                 // partial tiles: column stride (floats)
+    // gates per pair (compile-time unless the activation set is generic)
+    constexpr int GC = ACT == 1 ? 4 : (ACT == 2 || ACT == 4) ? 3 : ACT == 3 ? 1 : 4;
     // P: pairs per thread and half, at most (1 or 2)
     constexpr int KH = KBR / 2;                  // k block where the other half is published
     // k block where the next product's flags are polled: after the publish
@@ -140,8 +143,8 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
     // short products wait for their flags right before they start.
     constexpr bool EARLY = 4 * MTH * NT * KBR >= 128;
     extern __shared__ float smem[];
-    float *red = smem;                           // [2 halves][4 waves][BTH][LDR] partial tiles
-    float *hst = red + 8 * BTH * LDR;            // [BT * U] h of each (row, unit) pair
+    float *red = smem;                           // [2 halves][4 waves][NTC][LDC] partial tiles
+    float *hst = red + 8 * NTC * LDC;            // [BT * U] h of each (row, unit) pair
     float *cst = hst + BT * a.U;                 // [BT * U] LSTM cell state
     int *lst = (int *)(cst + BT * a.U);          // [BT] sequence length of each row
     float *cst_u = (float *)(lst + BT);          // [11][U] Wb, Rb per gate, then Pi, Po, Pf
@@ -235,17 +238,42 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
             const int i = tid + 256 * k;
             pk[h][k] = i < hpairs_of(h) ? ((h * BTH + i / uc) << 16) | (i % uc) : -1;
         }
+    // A thread keeps its pairs for the whole launch: their h, c, length,
+    // per-unit constants and output offsets live in registers.
+    const int G = ACT == 0 ? a.G : GC;
+    const size_t xstep = (size_t)a.Bt * GH;      // XW: one step
+    const size_t ystep = a.layout == 0 ? (size_t)a.D * a.Bt * a.H : (size_t)a.D * a.H;
+    float hreg[2][P], creg[2][P], kc[2][P][11];
+    int lreg[2][P];
+    uint32_t hoff[2][P];                         // offset of the pair in an H plane (from drow)
+    size_t xoff[2][P], yoff[2][P];               // offsets of the pair's XW and Y at step 0
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            const int rl = pk[h][k] < 0 ? 0 : pk[h][k] >> 16, u = pk[h][k] < 0 ? 0 : pk[h][k] & 0xffff;
+            const int pi = rl * uc + u;
+            const int b = row0 + rl, gu = u0 + u;
+            hreg[h][k] = hst[pi];
+            creg[h][k] = cst[pi];
+            lreg[h][k] = pk[h][k] < 0 ? 0 : lst[rl];
+#pragma unroll
+            for (int e = 0; e < 11; ++e)
+                kc[h][k][e] = cst_u[e * a.U + u];
+            hoff[h][k] = (uint32_t)(rl * Hp + gu);
+            xoff[h][k] = xwd + (size_t)(row0 + rl) * GH + u;
+            yoff[h][k] = a.layout == 0 ? ((size_t)d * a.Bt + b) * a.H + gu
+                                       : ((size_t)b * a.S * a.D + d) * a.H + gu;
+        }
     auto fetch_xw_q = [&](int qq, int h, int k, float *xv) {
         xv[0] = xv[1] = xv[2] = xv[3] = 0.0f;
-        const int rl = pk[h][k] >> 16, u = pk[h][k] & 0xffff;
-        const int len = lst[rl];
-        if (qq >= len)
+        if (qq >= lreg[h][k])
             return;
         // XW is stored by step (reverse included)
-        const float *src = a.XW + xwd + ((size_t)(qq - a.j_base) * a.Bt + row0 + rl) * GH + u;
+        const float *src = a.XW + xoff[h][k] + (size_t)(qq - a.j_base) * xstep;
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-            if (g < a.G)
+            if (g < G)
                 xv[g] = src[g * uc];
     };
     float xw_next[2][P][4];
@@ -297,7 +325,7 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
     for (int q = a.q_begin; q < a.q_end; ++q) {
         const int j = q;                         // one phase per step
         const int pj1 = next_plane(pj);
-        float *hnext = a.hbuf + (size_t)pj1 * plane + drow;
+        float *hnext = a.hbuf + (size_t)pj1 * plane + drow;   // (+ hoff: the pair)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int hrow0 = h * BTH;
@@ -348,14 +376,14 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
             };
             product_res_hooked<MTH, NT, KBR, kPipePrefetch, KH, KP>(
                 acc, ring, a_src(pj, h), Hp, rr, prefetch_xw, publish, poll_next);
-            float *redh = red + h * 4 * BTH * LDR;
+            // partial tiles, column-major: a lane's four rows of a column are
+            // contiguous (one 16-byte store per tile)
+            float *redh = red + h * 4 * NTC * LDC;
 #pragma unroll
             for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        redh[(w * BTH + mt * 16 + 4 * lq + r) * LDR + nt * 16 + lr] = acc[mt][nt][r];
+                    *(f4 *)(redh + (w * NTC + nt * 16 + lr) * LDC + mt * 16 + 4 * lq) = acc[mt][nt];
             __syncthreads();
             // if they were all set, load the next product's first k blocks now,
             // so that their latency overlaps this half's gate arithmetic;
@@ -366,6 +394,8 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
                 prime_ring<MTH, KBR, kPipePrefetch>(ring, a_src(h == 0 ? pj : pj1, nh), Hp);
 
             // ---- gate arithmetic of this thread's pairs of half h -------------
+            // (computed for every pair and kept only while the row is active,
+            // so that no branch separates the loads from their use)
             auto run_pairs = [&](auto F, auto Gf, auto Hf) {
 #pragma unroll
                 for (int k = 0; k < P; ++k) {
@@ -373,37 +403,37 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
                         continue;
                     const int rl = pk[h][k] >> 16, u = pk[h][k] & 0xffff;
                     const int rh = rl - hrow0;
-                    const int pi = rl * uc + u;
-                    const int b = row0 + rl;
-                    const int gu = u0 + u;
-                    const int len = lst[rl];
-                    const bool active = j < len;
-                    const float hp = hst[pi];
-                    float hn = hp, cn = cst[pi];
-                    if (active) {
-                        const float *rp = redh + rh * LDR + u;
-                        hn = gates_one_phase(
-                            op, xw[k],
-                            [&](int g) {
-                                const float *p = rp + g * uc;
-                                float v = p[0];
+                    // the four waves' partial sums of each gate column, all
+                    // loaded before the first is used
+                    float part[4][4];
+                    const float *rp = redh + u * LDC + rh;
 #pragma unroll
-                                for (int w2 = 1; w2 < 4; ++w2)
-                                    v = v + p[w2 * BTH * LDR];   // fixed wave order
-                                return v;
-                            },
-                            cst_u, a.U, u, Pd != nullptr, a.clip_on, a.clip, a.input_forget != 0,
-                            hp, cn, F, Gf, Hf);
-                    }
-                    store_coherent(hnext + (size_t)rl * Hp + gu, hn);   // carried when inactive
-                    hst[pi] = hn;
-                    cst[pi] = cn;
+                    for (int g = 0; g < 4; ++g)
+#pragma unroll
+                        for (int w2 = 0; w2 < 4; ++w2)
+                            part[g][w2] = g < G ? rp[(w2 * NTC + g * uc) * LDC] : 0.0f;
+                    const int len = lreg[h][k];
+                    const bool active = j < len;
+                    const float hp = hreg[h][k], cp = creg[h][k];
+                    float cx = cp;
+                    const float hx = gates_one_phase(
+                        op, xw[k],
+                        [&](int g) {
+                            float v = part[g][0];
+#pragma unroll
+                            for (int w2 = 1; w2 < 4; ++w2)
+                                v = v + part[g][w2];    // fixed wave order
+                            return v;
+                        },
+                        [&](int e) { return kc[h][k][e]; }, Pd != nullptr, a.clip_on, a.clip,
+                        a.input_forget != 0, hp, cx, F, Gf, Hf);
+                    const float hn = active ? hx : hp;   // carried when inactive
+                    hreg[h][k] = hn;
+                    creg[h][k] = active ? cx : cp;
+                    store_coherent(hnext + hoff[h][k], hn);
                     if (a.Y) {
                         const int t = active ? (rev ? len - 1 - j : j) : j;
-                        const size_t yo = a.layout == 0
-                                              ? (((size_t)t * a.D + d) * a.Bt + b) * a.H + gu
-                                              : (((size_t)b * a.S + t) * a.D + d) * a.H + gu;
-                        a.Y[yo] = active ? canon_nan(hn) : 0.0f;
+                        a.Y[yoff[h][k] + (size_t)t * ystep] = active ? canon_nan(hn) : 0.0f;
                     }
                 }
             };
@@ -434,7 +464,16 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
     }
 
     // ---- end of this launch: keep or publish the states ----------------------
-    __syncthreads();                             // (pairs were owned per half above)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int k = 0; k < P; ++k)
+            if (pk[h][k] >= 0) {
+                const int pi = (pk[h][k] >> 16) * uc + (pk[h][k] & 0xffff);
+                hst[pi] = hreg[h][k];
+                cst[pi] = creg[h][k];
+            }
+    __syncthreads();                             // (the loop below maps pairs to threads anew)
     const bool done = a.q_end == a.S;
     for (int pi = tid; pi < npairs; pi += 256) {
         const int rl = pi / uc, u = pi - rl * uc;
