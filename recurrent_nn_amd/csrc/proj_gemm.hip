@@ -90,6 +90,19 @@ __device__ __forceinline__ u4 load8h(const uint16_t *__restrict__ p, int64_t row
     return v;
 }
 
+// Buffer resource over `bytes` bytes at p (raw, 32-bit offsets; a load at
+// an offset at or past `bytes` returns zeros).  Word 3 is the gfx9 default
+// (32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Offset that no buffer here reaches (buffers of the fast path are smaller
+// than 2 GiB, and a stage adds at most K * 4 < 2 GiB bytes).
+constexpr uint32_t kOffNone = 0x80000000u;
+
 __device__ __forceinline__ u4 pack8(f4 a, f4 b)
 {
     u4 v;
@@ -185,6 +198,16 @@ __global__ void __launch_bounds__(256, 3) proj_gemm_kernel(ProjArgs a)
     const int64_t nk = (a.K + KS - 1) / KS;
     const bool a_vec = BF16 ? (a.K % 4 == 0) : (a.K % 4 == 0);
     const bool b_vec = BF16 ? (a.K % 8 == 0) : (a.K % 4 == 0);
+    // Stages whose k range lies inside K are loaded with buffer loads from
+    // row offsets computed once (rows that do not exist read as zeros); the
+    // partial last stage, and operands of 2 GiB or more, take the checked
+    // loads.
+    constexpr int ESZ = BF16 ? 2 : 4;
+    const int64_t a_bytes = BF16 ? a.D * Md * a.K * 2 : a.S * a.Bt * a.K * 4;
+    const int64_t b_bytes = a.GH * a.K * ESZ;
+    const bool fast = (BF16 ? a.K % 8 == 0 : a.K % 4 == 0) && a_bytes < (int64_t)kOffNone &&
+                      b_bytes < (int64_t)kOffNone;
+    const int64_t nk_fast = fast ? a.K / KS : 0;
 
     // staging: thread -> (row = tid / 8 + 32 i, chunk = tid % 8 of 16 bytes)
     const int srow = tid >> 3, sch = tid & 7;
@@ -198,8 +221,27 @@ __global__ void __launch_bounds__(256, 3) proj_gemm_kernel(ProjArgs a)
     if (!__syncthreads_or(any))
         return;                                      // no row of this tile is ever read
     const char *Wd = (const char *)a.Wp + (size_t)d * a.GH * a.K * (BF16 ? 2 : 4);
+    __amdgpu_buffer_rsrc_t rsa = buffer_of(BF16 ? (const void *)a.Xb : a.X, (uint32_t)(fast ? a_bytes : 0));
+    __amdgpu_buffer_rsrc_t rsb = buffer_of(Wd, (uint32_t)(fast ? b_bytes : 0));
+    uint32_t aoff[4], boff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t row = srow + 32 * i;
+        const int64_t ar = BF16 ? (m0 + row < Md ? d * Md + m0 + row : -1) : xr[i];
+        aoff[i] = ar >= 0 ? (uint32_t)(ar * a.K * ESZ) + sch * 16 : kOffNone;
+        boff[i] = n0 + row < a.GH ? (uint32_t)((n0 + row) * a.K * ESZ) + sch * 16 : kOffNone;
+    }
     u4 ra[4], rb[4];
     auto gload = [&](int64_t kt, u4 (&ra)[4], u4 (&rb)[4]) {
+        if (kt < nk_fast) {
+            const uint32_t kb = (uint32_t)kt * (KS * ESZ);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ra[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rsa, aoff[i] + kb, 0, 0));
+                rb[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rsb, boff[i] + kb, 0, 0));
+            }
+            return;
+        }
         const int64_t kbase = kt * KS;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
