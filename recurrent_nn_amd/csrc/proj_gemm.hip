@@ -232,16 +232,15 @@ __global__ void __launch_bounds__(256, 3) proj_gemm_kernel(ProjArgs a)
         boff[i] = n0 + row < a.GH ? (uint32_t)((n0 + row) * a.K * ESZ) + sch * 16 : kOffNone;
     }
     u4 ra[4], rb[4];
-    auto gload = [&](int64_t kt, u4 (&ra)[4], u4 (&rb)[4]) {
-        if (kt < nk_fast) {
-            const uint32_t kb = (uint32_t)kt * (KS * ESZ);
+    auto gload_fast = [&](uint32_t kt, u4 (&ra)[4], u4 (&rb)[4]) {
+        const uint32_t kb = kt * (KS * ESZ);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ra[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rsa, aoff[i] + kb, 0, 0));
-                rb[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rsb, boff[i] + kb, 0, 0));
-            }
-            return;
+        for (int i = 0; i < 4; ++i) {
+            ra[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rsa, aoff[i] + kb, 0, 0));
+            rb[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rsb, boff[i] + kb, 0, 0));
         }
+    };
+    auto gload = [&](int64_t kt, u4 (&ra)[4], u4 (&rb)[4]) {
         const int64_t kbase = kt * KS;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -309,10 +308,22 @@ __global__ void __launch_bounds__(256, 3) proj_gemm_kernel(ProjArgs a)
     };
     // one LDS buffer: the next stage waits in registers while this one is
     // consumed, then replaces it between two barriers
-    gload(0, ra, rb);
+    // (whole stages first, then the checked ones)
+    const int nkf = (int)nk_fast;
+    if (nkf > 0)
+        gload_fast(0, ra, rb);
+    else
+        gload(0, ra, rb);
     sstore(0, ra, rb);
     __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
+    for (int kt = 0; kt + 1 < nkf; ++kt) {
+        gload_fast(kt + 1, ra, rb);
+        stage(0);
+        __syncthreads();
+        sstore(0, ra, rb);
+        __syncthreads();
+    }
+    for (int64_t kt = nkf > 0 ? nkf - 1 : 0; kt < nk; ++kt) {
         if (kt + 1 < nk)
             gload(kt + 1, ra, rb);
         stage(0);
