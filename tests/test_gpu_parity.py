@@ -181,6 +181,39 @@ FEATURES = [
 ]
 
 
+# Projection staging: whole k stages (buffer loads), a partial last stage
+# (checked loads) and inputs whose K is not a multiple of the 16-byte load
+# (checked loads only), for both operand types, with ragged M and N tiles.
+# The bf16 cases are held to the fp32 bar against the oracle run with the
+# same bf16 rounding of X and W.
+STAGING = [
+    dict(op="GRU", direction="forward", S=5, Bt=50, I=100, H=70, linear_before_reset=0,
+         with_lens=True),                                  # fp32: 3 whole stages + 4
+    dict(op="GRU", direction="reverse", S=6, Bt=40, I=72, H=96, linear_before_reset=1,
+         with_lens=True, proj_bf16=True),                  # bf16: 1 whole stage + 8
+    dict(op="LSTM", direction="bidirectional", S=5, Bt=20, I=30, H=64, with_lens=True,
+         proj_bf16=True),                                  # bf16: K % 8 != 0
+    dict(op="RNN", direction="forward", S=9, Bt=130, I=136, H=40, layout=1,
+         proj_bf16=True),                                  # bf16: 2 whole stages + 8, 3 batch blocks
+    dict(op="LSTM", direction="forward", S=4, Bt=8, I=256, H=130, with_p=True,
+         proj_bf16=True),                                  # bf16: whole stages only
+]
+
+
+@pytest.mark.parametrize("k", range(len(STAGING)))
+def test_projection_staging_cases_match_oracle(k):
+    spec = dict(STAGING[k])
+    op, direction = spec.pop("op"), spec.pop("direction")
+    S, Bt, I, H = spec.pop("S"), spec.pop("Bt"), spec.pop("I"), spec.pop("H")
+    lay = spec.pop("layout", 0)
+    kw = {key: spec.pop(key) for key in ("with_lens", "with_p") if key in spec}
+    c = workloads.random_case(op, direction, S, Bt, I, H, seed=700 + k, layout=lay,
+                              with_h0=True, with_c0=(op == "LSTM"),
+                              scale=min(0.6, 1.5 / H ** 0.5), **kw, **spec)
+    say(f"case {c.name} {STAGING[k]}")
+    compare(c, run_gpu(c))
+
+
 @pytest.mark.parametrize("k", range(len(FEATURES)))
 def test_feature_cases_match_oracle(k):
     spec = dict(FEATURES[k])
