@@ -12,8 +12,13 @@
 //     (plain VALU arithmetic; no matrix cores, no split of k), so the value
 //     does not depend on the tiling or the grid;
 //   - the activations are the exact-mode ones (exact_math.h).
-// Each phase stages k-chunks of the block's H rows and R rows in LDS; thread
-// t owns column t % NTC of the block and rows t / NTC + rpp * i.
+// Each phase stages k-chunks of the block's H rows and R rows in LDS (the
+// next chunk is loaded into registers while the current one is consumed);
+// thread t owns columns c and c + NTC/2 of the block, c = t % (NTC/2), and
+// rows t / (NTC/2) + rpp * i, i < NACC, all in registers, and reads four
+// consecutive k of its H rows and R rows per LDS access.  Summing the padding columns [H, Hp) (zeros in H and
+// in the packed R) adds +0 to a sum that started at +0, which leaves it
+// unchanged: such a sum is never -0.
 #pragma once
 
 #include "exact_math.h"
@@ -21,27 +26,41 @@
 
 namespace rnnamd {
 
-constexpr int kExactKT = 32;        // k values per staged chunk
-constexpr int kExactMaxAcc = 32;    // accumulators per thread (rows per pass)
+constexpr int kExactKT = 32;        // k values per staged chunk (Hp is a multiple)
+constexpr int kExactKTP = kExactKT + 4;   // LDS row stride (floats)
 
-// LDS bytes: H chunk [BT][KT+1], R chunk [NTC][KT+1], the sums [BT][NTC],
+// LDS bytes: H chunk [BT][KTP], R chunk [NTC][KTP], the sums [BT][NTC],
 // then h, c, z per pair, lengths, per-unit constants.
 __host__ __device__ inline size_t rec_exact_lds_bytes(int bt, int nt, int u)
 {
     const size_t ntc = (size_t)nt * 16;
-    return (bt * (size_t)(kExactKT + 1) + ntc * (kExactKT + 1) + (size_t)bt * ntc +
+    return (bt * (size_t)kExactKTP + ntc * kExactKTP + (size_t)bt * ntc +
             3 * (size_t)bt * u + bt + 11 * (size_t)u) * 4;
 }
 
+// Rows per thread for a block of bt rows and ntc columns (two columns per
+// thread): the rows per pass rpp = 256 / (ntc / 2), and ceil(bt / rpp)
+// rounded up to a power of two.
+__host__ __device__ inline int rec_exact_nacc(int bt, int ntc)
+{
+    const int rpp = 256 / (ntc / 2);
+    const int need = (bt + rpp - 1) / rpp;
+    int n = 1;
+    while (n < need)
+        n *= 2;
+    return n;
+}
+
+template <int NACC>
 __global__ void __launch_bounds__(256, 1) rec_exact_kernel(RecArgs a)
 {
-    constexpr int KT = kExactKT;
+    constexpr int KT = kExactKT, KTP = kExactKTP;
     const int BT = a.BT;
     const int NTC = a.NT * 16;
-    extern __shared__ float smem[];
-    float *hs = smem;                            // [BT][KT+1]  H rows, one k chunk
-    float *rs = hs + BT * (KT + 1);              // [NTC][KT+1] R rows, one k chunk
-    float *red = rs + NTC * (KT + 1);            // [BT][NTC]   the products of this phase
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    float *hs = smem;                            // [BT][KTP]  H rows, one k chunk
+    float *rs = hs + BT * KTP;                   // [NTC][KTP] R rows, one k chunk
+    float *red = rs + NTC * KTP;                 // [BT][NTC]   the products of this phase
     float *hst = red + BT * NTC;                 // [BT * U]
     float *cst = hst + BT * a.U;
     float *zst = cst + BT * a.U;
@@ -106,11 +125,17 @@ __global__ void __launch_bounds__(256, 1) rec_exact_kernel(RecArgs a)
         __syncthreads();
     }
 
-    // thread -> (column c, rows r0 + rpp * i)
-    const int rpp = 256 / NTC;                   // rows per pass (NTC <= 128)
-    const int c = tid % NTC;
-    const int r0 = tid / NTC;
+    // thread -> (columns c, c + NC2; rows r0 + rpp * i)
+    const int NC2 = NTC / 2;
+    const int rpp = 256 / NC2;                   // rows per pass (NTC <= 128)
+    const int c = tid % NC2;
+    const int r0 = tid / NC2;
     const bool worker = r0 < rpp;
+    // staging: H chunk = BT rows x KT/4 float4, R chunk = ncol rows x KT/4
+    constexpr int Q = KT / 4;                    // float4 per row and chunk
+    constexpr int SH = 64 * Q / 256;             // H float4 per thread (BT <= 64)
+    constexpr int SR = 128 * Q / 256;            // R float4 per thread (ncol <= 128)
+    const int nchunks = Hp / KT;
 
     bool dead = false;
     for (int q = a.q_begin; q < a.q_end; ++q) {
@@ -122,47 +147,81 @@ __global__ void __launch_bounds__(256, 1) rec_exact_kernel(RecArgs a)
         const int ncol = (ph == 0 ? a.NTA : a.NTB) * 16;
         const float *asrc = (ph == 0 ? a.hbuf + (size_t)(j % ring_n) * plane
                                      : a.sbuf + (size_t)(j % a.xw_steps) * plane) + drow;
+        const float *rsrc = rblk + (size_t)cb * Hp;
 
         // ---- the product, one accumulator per output, k increasing --------
-        for (int rbase = 0; rbase < rows; rbase += rpp * kExactMaxAcc) {
-            // accumulators in use this pass (the same for the whole workgroup)
-            const int nacc = min(kExactMaxAcc, (rows - rbase + rpp - 1) / rpp);
-            float acc[kExactMaxAcc];
+        f4 hreg[SH], rreg[SR];
+        auto gload = [&](int kc) {
+            const int k0 = kc * KT;
 #pragma unroll
-            for (int i = 0; i < kExactMaxAcc; ++i)
-                acc[i] = 0.0f;
-            for (int k0 = 0; k0 < a.H; k0 += KT) {
-                const int kn = min(KT, a.H - k0);
-                __syncthreads();                 // the previous chunk is consumed
-                for (int e = tid; e < rows * KT; e += 256) {
-                    const int rl = e / KT, kk = e - rl * KT;
-                    hs[rl * (KT + 1) + kk] = kk < kn ? asrc[(size_t)rl * Hp + k0 + kk] : 0.0f;
-                }
-                for (int e = tid; e < ncol * KT; e += 256) {
-                    const int cl = e / KT, kk = e - cl * KT;
-                    rs[cl * (KT + 1) + kk] = kk < kn ? rblk[(size_t)(cb + cl) * Hp + k0 + kk] : 0.0f;
-                }
-                __syncthreads();
-                if (worker && c < ncol) {
-                    for (int kk = 0; kk < kn; ++kk) {
-                        const float rv = rs[c * (KT + 1) + kk];
+            for (int i = 0; i < SH; ++i) {
+                const int e = tid + 256 * i, rl = e / Q, kq = e - rl * Q;
+                if (rl < BT)
+                    hreg[i] = *(const f4 *)(asrc + (size_t)rl * Hp + k0 + 4 * kq);
+            }
 #pragma unroll
-                        for (int i = 0; i < kExactMaxAcc; ++i) {
-                            if (i >= nacc)
-                                break;
-                            const int rl = rbase + r0 + rpp * i;   // rows >= `rows`: never stored
-                            const float pr = __fmul_rn(hs[min(rl, BT - 1) * (KT + 1) + kk], rv);
-                            acc[i] = __fadd_rn(acc[i], pr);
+            for (int i = 0; i < SR; ++i) {
+                const int e = tid + 256 * i, cl = e / Q, kq = e - cl * Q;
+                if (cl < ncol)
+                    rreg[i] = *(const f4 *)(rsrc + (size_t)cl * Hp + k0 + 4 * kq);
+            }
+        };
+        auto sstore = [&]() {
+#pragma unroll
+            for (int i = 0; i < SH; ++i) {
+                const int e = tid + 256 * i, rl = e / Q, kq = e - rl * Q;
+                if (rl < BT)
+                    *(f4 *)(hs + rl * KTP + 4 * kq) = hreg[i];
+            }
+#pragma unroll
+            for (int i = 0; i < SR; ++i) {
+                const int e = tid + 256 * i, cl = e / Q, kq = e - cl * Q;
+                if (cl < ncol)
+                    *(f4 *)(rs + cl * KTP + 4 * kq) = rreg[i];
+            }
+        };
+        float acc[NACC], acc2[NACC];
+#pragma unroll
+        for (int i = 0; i < NACC; ++i)
+            acc[i] = acc2[i] = 0.0f;
+        // rows past the block's BT read row BT - 1; their sums are never stored
+        int hrow[NACC];
+#pragma unroll
+        for (int i = 0; i < NACC; ++i)
+            hrow[i] = min(r0 + rpp * i, BT - 1) * KTP;
+        const bool computes = worker && c < ncol;
+        gload(0);
+        for (int kc = 0; kc < nchunks; ++kc) {
+            __syncthreads();                     // the previous chunk is consumed
+            sstore();
+            __syncthreads();
+            if (kc + 1 < nchunks)
+                gload(kc + 1);
+            if (computes) {
+#pragma unroll 2
+                for (int kk = 0; kk < KT; kk += 4) {
+                    const f4 rv = *(const f4 *)(rs + c * KTP + kk);
+                    const f4 rv2 = *(const f4 *)(rs + (c + NC2) * KTP + kk);
+#pragma unroll
+                    for (int i = 0; i < NACC; ++i) {
+                        const f4 hv = *(const f4 *)(hs + hrow[i] + kk);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            acc[i] = __fadd_rn(acc[i], __fmul_rn(hv[e], rv[e]));
+                            acc2[i] = __fadd_rn(acc2[i], __fmul_rn(hv[e], rv2[e]));
                         }
                     }
                 }
             }
-            if (worker && c < ncol) {
+        }
+        if (computes) {
 #pragma unroll
-                for (int i = 0; i < kExactMaxAcc; ++i) {
-                    const int rl = rbase + r0 + rpp * i;
-                    if (rl < rows)
-                        red[rl * NTC + cb + c] = acc[i];
+            for (int i = 0; i < NACC; ++i) {
+                const int rl = r0 + rpp * i;
+                if (rl < rows) {
+                    red[rl * NTC + cb + c] = acc[i];
+                    if (c + NC2 < ncol)
+                        red[rl * NTC + cb + c + NC2] = acc2[i];
                 }
             }
         }
