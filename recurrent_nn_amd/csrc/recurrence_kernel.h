@@ -130,32 +130,26 @@ __device__ __forceinline__ void product_res(f4 (&acc)[MT][NT], const float *asrc
     }
 }
 
-// The same with R streamed from memory every step (runtime KB).
+// The same with R streamed from memory every step (runtime KB).  Two
+// register sets alternate: block kb + 1 is loaded while block kb is
+// multiplied.  The loop body has no branch and no register copies, so the
+// compiler's wait before a block's MFMAs covers that block's loads only (a
+// copy of the prefetched block at the end of each iteration made it wait
+// for the loads just issued, every block).
 template <int MT, int NT, int T0, int T1, typename Mid>
 __device__ __forceinline__ void product_stream(f4 (&acc)[MT][NT], const float *asrc,
                                                const float *rfrag, int Hp, int KB, Mid mid)
 {
-    f4 av[MT], bv[NT];
+    f4 a0[MT], b0[NT], a1[MT], b1[NT];
+    auto load = [&](f4 (&av)[MT], f4 (&bv)[NT], int kb) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-        av[mt] = *(const f4 *)(asrc + (size_t)mt * 16 * Hp);
+        for (int mt = 0; mt < MT; ++mt)
+            av[mt] = *(const f4 *)(asrc + (size_t)mt * 16 * Hp + kb * 16);
 #pragma unroll
-    for (int nt = T0; nt < T1; ++nt)
-        bv[nt] = *(const f4 *)(rfrag + (size_t)nt * 16 * Hp);
-    if (KB == 1)
-        mid();
-    for (int kb = 0; kb < KB; ++kb) {
-        f4 an[MT], bn[NT];
-        if (kb + 1 < KB) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                an[mt] = *(const f4 *)(asrc + (size_t)mt * 16 * Hp + (kb + 1) * 16);
-#pragma unroll
-            for (int nt = T0; nt < T1; ++nt)
-                bn[nt] = *(const f4 *)(rfrag + (size_t)nt * 16 * Hp + (kb + 1) * 16);
-            if (kb + 2 == KB)
-                mid();
-        }
+        for (int nt = T0; nt < T1; ++nt)
+            bv[nt] = *(const f4 *)(rfrag + (size_t)nt * 16 * Hp + kb * 16);
+    };
+    auto mma = [&](const f4 (&av)[MT], const f4 (&bv)[NT]) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -166,14 +160,23 @@ __device__ __forceinline__ void product_stream(f4 (&acc)[MT][NT], const float *a
                                                                        acc[mt][nt], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);   // keep the independent accumulators together
         }
-        if (kb + 1 < KB) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                av[mt] = an[mt];
-#pragma unroll
-            for (int nt = T0; nt < T1; ++nt)
-                bv[nt] = bn[nt];
-        }
+    };
+    load(a0, b0, 0);
+    int kb = 0;
+    for (; kb + 2 < KB; kb += 2) {
+        load(a1, b1, kb + 1);
+        mma(a0, b0);
+        load(a0, b0, kb + 2);
+        mma(a1, b1);
+    }
+    if (KB - kb == 2) {                          // two blocks left
+        load(a1, b1, kb + 1);
+        mid();
+        mma(a0, b0);
+        mma(a1, b1);
+    } else {                                     // one block left
+        mid();
+        mma(a0, b0);
     }
 }
 
