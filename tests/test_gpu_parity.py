@@ -178,6 +178,10 @@ FEATURES = [
     dict(op="GRU", direction="forward", S=4, Bt=2, I=3, H=7, with_bias=False, with_h0=False,
          linear_before_reset=1, activations=["Sigmoid", "ScaledTanh"], alpha=[1.3], beta=[0.6]),
     dict(op="LSTM", direction="forward", S=24, Bt=32, I=64, H=512, with_lens=True),
+    # R streamed with an odd number of k blocks per wave (5 and 7)
+    dict(op="RNN", direction="reverse", S=5, Bt=24, I=16, H=300, with_lens=True),
+    dict(op="GRU", direction="forward", S=4, Bt=40, I=24, H=420, linear_before_reset=1,
+         with_lens=True),
 ]
 
 
