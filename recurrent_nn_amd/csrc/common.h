@@ -141,6 +141,7 @@ struct InitArgs {
     const float *h0, *c0;       // nullable, layout-dependent
     float *hbuf, *sbuf, *cbuf;  // sbuf/cbuf nullable
     int32_t *lens_dev;
+    const int32_t *order;       // [Bt] batch row held at each position, or NULL (identity)
     int32_t fill_lens;          // >= 0: every row gets this length (sequence_lens absent)
     uint32_t *bar;
     int64_t n_bar;
@@ -179,7 +180,11 @@ struct RecArgs {
     ActSpec act[2][3];
     // buffers
     const float *Rp, *XW, *B, *P;
-    const int32_t *lens;
+    // Rows are held in order of decreasing length: position s holds batch
+    // row order[s] (identity when order is NULL), lens[s] is its length, and
+    // the H history, cell state and XW rows use positions; only the outputs
+    // Y, Y_h, Y_c use batch rows.
+    const int32_t *lens, *order;
     float *hbuf, *sbuf, *cbuf, *zbuf;
     float *Y, *Yh, *Yc;
     uint32_t *bar;

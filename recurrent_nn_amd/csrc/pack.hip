@@ -131,10 +131,12 @@ __global__ void init_kernel(InitArgs a)
         float v = 0.0f;
         if (a.h0) {
             const int64_t k = i % a.Hp;
-            const int64_t b = (i / a.Hp) % a.Btp;
+            const int64_t s = (i / a.Hp) % a.Btp;    // position; batch row order[s]
             const int64_t d = i / (a.Hp * a.Btp);
-            if (b < a.Bt && k < a.H)
+            if (s < a.Bt && k < a.H) {
+                const int64_t b = a.order ? a.order[s] : s;
                 v = a.layout == 0 ? a.h0[(d * a.Bt + b) * a.H + k] : a.h0[(b * a.D + d) * a.H + k];
+            }
         }
         a.hbuf[i] = v;
     }
@@ -144,7 +146,8 @@ __global__ void init_kernel(InitArgs a)
             float v = 0.0f;
             if (a.c0) {
                 const int64_t k = i % a.H;
-                const int64_t b = (i / a.H) % a.Bt;
+                const int64_t s = (i / a.H) % a.Bt;
+                const int64_t b = a.order ? a.order[s] : s;
                 const int64_t d = i / (a.H * a.Bt);
                 v = a.layout == 0 ? a.c0[(d * a.Bt + b) * a.H + k] : a.c0[(b * a.D + d) * a.H + k];
             }

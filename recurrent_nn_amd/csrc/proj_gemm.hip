@@ -4,14 +4,15 @@
 // in block-column order, see pack.hip), so XW comes out in the order the
 // recurrence reads it.
 //
-// Rows.  XW is stored by STEP: row (j - j_base, b) of direction d holds the
-// projection of the X row that step j of batch row b reads -- time j
-// forward, len_b - 1 - j in reverse ("Choices the specification leaves
+// Rows.  Batch rows are held in order of decreasing length (position i
+// holds batch row order[i]), so that rows the step loop never reads cluster.
+// XW is stored by STEP: row (j - j_base, i) of direction d holds the
+// projection of the X row that step j of the row at position i reads -- time
+// j forward, len_b - 1 - j in reverse ("Choices the specification leaves
 // open": sequence_lens and reverse traversal) -- for the steps of one time
 // chunk.  Rows the step loop never reads (j >= len_b) are not computed: a
-// tile whose rows are all such is skipped, and batch rows are visited in
-// order of decreasing length so that they cluster.  Both directions are one
-// launch (the direction is part of the tile index).
+// tile whose rows are all such is skipped.  Both directions are one launch
+// (the direction is part of the tile index).
 //
 // Tiling: 128x128 output tile per 256-thread workgroup, 4 waves of 64x64, K
 // staged through LDS in 128-byte row slices (32 fp32 or 64 bf16 values): the
@@ -114,15 +115,15 @@ __device__ __forceinline__ u4 pack8(f4 a, f4 b)
 }
 
 // X row read by logical row m = (j - j_base) * Bt + i of direction d, i.e.
-// step j of batch row order[i]; -1 when the step loop never reads it
+// step j of the batch row at position i; -1 when the step loop never reads it
 // (j >= len) or m is past the chunk.
 __device__ __forceinline__ int64_t proj_xrow(const ProjArgs &a, int64_t d, int64_t m)
 {
     if (m >= a.steps * a.Bt)
         return -1;
     const uint32_t jl = (uint32_t)m / (uint32_t)a.Bt, i = (uint32_t)m - jl * (uint32_t)a.Bt;
-    const int64_t b = a.order ? a.order[i] : i;
-    const int64_t j = a.j_base + jl, len = a.lens[b];
+    const int64_t b = a.order ? a.order[i] : i;          // position i holds batch row b
+    const int64_t j = a.j_base + jl, len = a.lens[i];
     if (j >= len)
         return -1;
     const int64_t t = (a.reverse_only || d == 1) ? len - 1 - j : j;
@@ -334,8 +335,8 @@ __global__ void __launch_bounds__(256, 3) proj_gemm_kernel(ProjArgs a)
         }
     }
 
-    // store: lane holds rows 4*lq + r, column lr of each 16x16 tile; logical
-    // row (j - j_base, i) goes to XW row (j - j_base, order[i])
+    // store: lane holds rows 4*lq + r, column lr of each 16x16 tile; row
+    // m = (j - j_base) * Bt + i is XW's row for step j, position i
     float *XWd = a.XW + (size_t)d * Md * a.GH;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -344,9 +345,7 @@ __global__ void __launch_bounds__(256, 3) proj_gemm_kernel(ProjArgs a)
             const int64_t m = m0 + wm * 64 + i * 16 + lq * 4 + r;
             if (m >= Md)
                 continue;
-            const uint32_t jl = (uint32_t)m / (uint32_t)a.Bt, ii = (uint32_t)m - jl * (uint32_t)a.Bt;
-            const size_t b = a.order ? (size_t)a.order[ii] : ii;
-            const size_t ro = ((size_t)jl * a.Bt + b) * a.GH;
+            const size_t ro = (size_t)m * a.GH;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t n = n0 + wn * 64 + j * 16 + lr;
@@ -438,9 +437,7 @@ __global__ void __launch_bounds__(256) proj_exact_kernel(ProjArgs a)
         const int64_t m = m0 + ty + 16 * i;
         if (m >= Md)
             continue;
-        const uint32_t jl = (uint32_t)m / (uint32_t)a.Bt, ii = (uint32_t)m - jl * (uint32_t)a.Bt;
-        const size_t b = a.order ? (size_t)a.order[ii] : ii;
-        const size_t ro = ((size_t)jl * a.Bt + b) * a.GH;
+        const size_t ro = (size_t)m * a.GH;     // step j - j_base, position i
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t n = n0 + tx + 16 * j;

@@ -102,11 +102,11 @@ __global__ void __launch_bounds__(256, 1) rec_exact_kernel(RecArgs a)
         const int j0 = a.q_begin / a.phases;
         for (int pi = tid; pi < npairs; pi += 256) {
             const int rl = pi / uc, u = pi - rl * uc;
-            const int b = row0 + rl;
+            const int s = row0 + rl;                      // position
             hst[pi] = a.hbuf[(size_t)(j0 % ring_n) * plane + drow + (size_t)rl * Hp + u0 + u];
-            cst[pi] = op == RNN_OP_LSTM ? a.cbuf[((size_t)d * a.Bt + b) * a.H + u0 + u] : 0.0f;
+            cst[pi] = op == RNN_OP_LSTM ? a.cbuf[((size_t)d * a.Bt + s) * a.H + u0 + u] : 0.0f;
             zst[pi] = (a.phases == 2 && (a.q_begin % 2) == 1)
-                          ? a.zbuf[((size_t)d * a.Bt + b) * a.H + u0 + u]
+                          ? a.zbuf[((size_t)d * a.Bt + s) * a.H + u0 + u]
                           : 0.0f;
         }
         for (int rl = tid; rl < rows; rl += 256)
@@ -232,7 +232,8 @@ __global__ void __launch_bounds__(256, 1) rec_exact_kernel(RecArgs a)
         float *snext = a.sbuf ? a.sbuf + (size_t)(j % a.xw_steps) * plane + drow : nullptr;
         for (int pi = tid; pi < npairs; pi += 256) {
             const int rl = pi / uc, u = pi - rl * uc;
-            const int b = row0 + rl;
+            const int s = row0 + rl;                      // position (XW row)
+            const int b = a.order ? a.order[s] : s;       // batch row (outputs)
             const int gu = u0 + u;
             const int len = lst[rl];
             const bool active = j < len;
@@ -240,7 +241,7 @@ __global__ void __launch_bounds__(256, 1) rec_exact_kernel(RecArgs a)
             float hn = hp, cn = cst[pi];
             float xv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             if (active) {
-                const float *src = a.XW + xwd + ((size_t)(j - a.j_base) * a.Bt + b) * GH + u;
+                const float *src = a.XW + xwd + ((size_t)(j - a.j_base) * a.Bt + s) * GH + u;
                 for (int g = 0; g < a.G; ++g)
                     xv[g] = src[g * uc];
             }
@@ -294,14 +295,16 @@ __global__ void __launch_bounds__(256, 1) rec_exact_kernel(RecArgs a)
     const bool done = a.q_end == a.S * a.phases;
     for (int pi = tid; pi < npairs; pi += 256) {
         const int rl = pi / uc, u = pi - rl * uc;
-        const int b = row0 + rl;
-        const size_t so = ((size_t)d * a.Bt + b) * a.H + u0 + u;
+        const int s = row0 + rl;
+        const int b = a.order ? a.order[s] : s;           // batch row (outputs)
+        const size_t so = ((size_t)d * a.Bt + s) * a.H + u0 + u;
         if (op == RNN_OP_LSTM)
             a.cbuf[so] = cst[pi];
         if (a.phases == 2)
             a.zbuf[so] = zst[pi];
         if (done) {
-            const size_t yo = a.layout == 0 ? so : ((size_t)b * a.D + d) * a.H + u0 + u;
+            const size_t yo = a.layout == 0 ? ((size_t)d * a.Bt + b) * a.H + u0 + u
+                                            : ((size_t)b * a.D + d) * a.H + u0 + u;
             const bool none = lst[rl] == 0;
             if (a.Yh)
                 a.Yh[yo] = none ? 0.0f : canon_nan(hst[pi]);

@@ -38,6 +38,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "activations.h"
 #include "common.h"
 
@@ -136,9 +138,29 @@ __device__ __forceinline__ void product_res(f4 (&acc)[MT][NT], const float *asrc
 // compiler's wait before a block's MFMAs covers that block's loads only (a
 // copy of the prefetched block at the end of each iteration made it wait
 // for the loads just issued, every block).
+// f(std::integral_constant<int, M>) with M = min(max(n, 0), N): the number
+// of row tiles, known at compile time, whose MFMAs a product issues.
+template <int N, typename F>
+__device__ __forceinline__ void with_row_tiles(int n, F f)
+{
+    if constexpr (N == 0) {
+        f(std::integral_constant<int, 0>{});
+    } else {
+        if (n >= N)
+            f(std::integral_constant<int, N>{});
+        else
+            with_row_tiles<N - 1>(n, f);
+    }
+}
+
+// mt_act: row tiles that hold a row still active at this step (rows are held
+// in order of decreasing length, so they form a prefix); the MFMAs of the
+// others are skipped, their sums are never read.  Every A tile is still
+// loaded, so that the loads do not depend on mt_act.
 template <int MT, int NT, int T0, int T1, typename Mid>
 __device__ __forceinline__ void product_stream(f4 (&acc)[MT][NT], const float *asrc,
-                                               const float *rfrag, int Hp, int KB, Mid mid)
+                                               const float *rfrag, int Hp, int KB, int mt_act,
+                                               Mid mid)
 {
     f4 a0[MT], b0[NT], a1[MT], b1[NT];
     auto load = [&](f4 (&av)[MT], f4 (&bv)[NT], int kb) {
@@ -150,16 +172,19 @@ __device__ __forceinline__ void product_stream(f4 (&acc)[MT][NT], const float *a
             bv[nt] = *(const f4 *)(rfrag + (size_t)nt * 16 * Hp + kb * 16);
     };
     auto mma = [&](const f4 (&av)[MT], const f4 (&bv)[NT]) {
+        with_row_tiles<MT>(mt_act, [&](auto mta) {
+            constexpr int MTA = decltype(mta)::value;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+            for (int s = 0; s < 4; ++s) {
 #pragma unroll
-            for (int nt = T0; nt < T1; ++nt)
+                for (int nt = T0; nt < T1; ++nt)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt][s], bv[nt][s],
-                                                                       acc[mt][nt], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);   // keep the independent accumulators together
-        }
+                    for (int mt = 0; mt < MTA; ++mt)
+                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt][s], bv[nt][s],
+                                                                           acc[mt][nt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);   // keep the independent accumulators together
+            }
+        });
     };
     load(a0, b0, 0);
     int kb = 0;
@@ -373,11 +398,11 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
         const int j0 = a.q_begin / a.phases;
         for (int pi = tid; pi < npairs; pi += kThreads) {
             const int rl = pi / uc, u = pi - rl * uc;
-            const int b = row0 + rl;
+            const int s = row0 + rl;                      // position
             hst[pi] = a.hbuf[(size_t)(j0 % (a.xw_steps + 1)) * plane + drow + (size_t)rl * Hp + u0 + u];
-            cst[pi] = op == RNN_OP_LSTM ? a.cbuf[((size_t)d * a.Bt + b) * a.H + u0 + u] : 0.0f;
+            cst[pi] = op == RNN_OP_LSTM ? a.cbuf[((size_t)d * a.Bt + s) * a.H + u0 + u] : 0.0f;
             zst[pi] = (a.phases == 2 && (a.q_begin % 2) == 1)
-                          ? a.zbuf[((size_t)d * a.Bt + b) * a.H + u0 + u]
+                          ? a.zbuf[((size_t)d * a.Bt + s) * a.H + u0 + u]
                           : 0.0f;
         }
         for (int rl = tid; rl < rows; rl += kThreads)
@@ -480,6 +505,14 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
         const float *asrc = (ph == 0 ? a.hbuf + (size_t)(j % (a.xw_steps + 1)) * plane
                                      : a.sbuf + (size_t)(j % a.xw_steps) * plane) + drow +
                             (size_t)lr * Hp + w * KB * 16 + 4 * lq;
+        // row tiles that hold a row still active at step j (the rows are held
+        // in order of decreasing length); the streamed product skips the
+        // MFMAs of the rest, whose sums are never read.  (The register-
+        // resident products issue every tile: their copies per tile count
+        // measured slower where all rows are active.)
+        int mt_act = MT;
+        if constexpr (!RES)
+            mt_act = (__popcll(__ballot(lane < rows && lst[lane] > j)) + 15) / 16;
         f4 acc[MT][NT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -495,9 +528,9 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
                 product_res<MT, NT, KBR, TA, NT, kPrefetch>(acc, asrc, Hp, rr, prefetch_xw);
         } else {
             if (ph == 0)
-                product_stream<MT, NT, 0, TA0>(acc, asrc, rfrag, Hp, KB, prefetch_xw);
+                product_stream<MT, NT, 0, TA0>(acc, asrc, rfrag, Hp, KB, mt_act, prefetch_xw);
             else if constexpr (TA > 0)
-                product_stream<MT, NT, TA, NT>(acc, asrc, rfrag, Hp, KB, prefetch_xw);
+                product_stream<MT, NT, TA, NT>(acc, asrc, rfrag, Hp, KB, mt_act, prefetch_xw);
         }
         // ---- partial tiles -> LDS, summed in wave order ----------------------
 #pragma unroll
@@ -525,7 +558,7 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
         float *snext = a.sbuf ? a.sbuf + (size_t)(j % a.xw_steps) * plane + drow : nullptr;
         auto do_pair = [&](int pi, const float *xv, auto F, auto Gf, auto Hf) {
             const int rl = pi / uc, u = pi - rl * uc;
-            const int b = row0 + rl;
+            const int b = a.order ? a.order[row0 + rl] : row0 + rl;   // batch row (outputs)
             const int gu = u0 + u;                         // hidden unit
             const int len = lst[rl];
             const bool active = j < len;
@@ -608,14 +641,16 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
     const bool done = a.q_end == a.S * a.phases;
     for (int pi = tid; pi < npairs; pi += kThreads) {
         const int rl = pi / uc, u = pi - rl * uc;
-        const int b = row0 + rl;
-        const size_t so = ((size_t)d * a.Bt + b) * a.H + u0 + u;
+        const int s = row0 + rl;
+        const int b = a.order ? a.order[s] : s;           // batch row (outputs)
+        const size_t so = ((size_t)d * a.Bt + s) * a.H + u0 + u;
         if (op == RNN_OP_LSTM)
             a.cbuf[so] = cst[pi];
         if (a.phases == 2)
             a.zbuf[so] = zst[pi];
         if (done) {
-            const size_t yo = a.layout == 0 ? so : ((size_t)b * a.D + d) * a.H + u0 + u;
+            const size_t yo = a.layout == 0 ? ((size_t)d * a.Bt + b) * a.H + u0 + u
+                                            : ((size_t)b * a.D + d) * a.H + u0 + u;
             const bool none = lst[rl] == 0;
             if (a.Yh)
                 a.Yh[yo] = none ? 0.0f : canon_nan(hst[pi]);

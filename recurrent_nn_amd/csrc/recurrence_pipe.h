@@ -253,7 +253,8 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
         for (int k = 0; k < P; ++k) {
             const int rl = pk[h][k] < 0 ? 0 : pk[h][k] >> 16, u = pk[h][k] < 0 ? 0 : pk[h][k] & 0xffff;
             const int pi = rl * uc + u;
-            const int b = row0 + rl, gu = u0 + u;
+            const int s = row0 + rl, gu = u0 + u;
+            const int b = a.order ? a.order[s] : s;       // batch row (outputs)
             hreg[h][k] = hst[pi];
             creg[h][k] = cst[pi];
             lreg[h][k] = pk[h][k] < 0 ? 0 : lst[rl];
@@ -477,12 +478,13 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
     const bool done = a.q_end == a.S;
     for (int pi = tid; pi < npairs; pi += 256) {
         const int rl = pi / uc, u = pi - rl * uc;
-        const int b = row0 + rl;
-        const size_t so = ((size_t)d * a.Bt + b) * a.H + u0 + u;
+        const int s = row0 + rl;
+        const int b = a.order ? a.order[s] : s;           // batch row (outputs)
         if (op == RNN_OP_LSTM)
-            a.cbuf[so] = cst[pi];
+            a.cbuf[((size_t)d * a.Bt + s) * a.H + u0 + u] = cst[pi];
         if (done) {
-            const size_t yo = a.layout == 0 ? so : ((size_t)b * a.D + d) * a.H + u0 + u;
+            const size_t yo = a.layout == 0 ? ((size_t)d * a.Bt + b) * a.H + u0 + u
+                                            : ((size_t)b * a.D + d) * a.H + u0 + u;
             const bool none = lst[rl] == 0;
             if (a.Yh)
                 a.Yh[yo] = none ? 0.0f : canon_nan(hst[pi]);

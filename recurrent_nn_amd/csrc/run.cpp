@@ -230,10 +230,12 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
     int32_t *lens_dev = (int32_t *)(ws + p->ws.lens);
     const int32_t *order_dev = nullptr;
     if (sequence_lens) {
-        // lengths and the batch rows in order of decreasing length (ties by
-        // row), staged in pinned memory owned by the plan
+        // the batch rows in order of decreasing length (ties by row) and
+        // their lengths in that order, staged in pinned memory owned by the
+        // plan: the kernels hold rows in this order, so that the rows still
+        // active at a step come first
         if (!p->lens_host) {
-            e = hipHostMalloc((void **)&p->lens_host, (size_t)p->Bt * 2 * sizeof(int32_t),
+            e = hipHostMalloc((void **)&p->lens_host, (size_t)p->Bt * 3 * sizeof(int32_t),
                               hipHostMallocDefault);
             if (e != hipSuccess)
                 return hip_fail(e, "hipHostMalloc (sequence_lens staging)");
@@ -249,12 +251,14 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
                 return hip_fail(e, "hipEventSynchronize (sequence_lens staging)");
             p->lens_pending = 0;
         }
-        int32_t *hl = p->lens_host, *ho = p->lens_host + p->Bt;
+        int32_t *hl = p->lens_host, *hs = hl + p->Bt, *ho = hl + 2 * p->Bt;
         std::memcpy(hl, sequence_lens, (size_t)p->Bt * sizeof(int32_t));
         for (int64_t b = 0; b < p->Bt; ++b)
             ho[b] = (int32_t)b;
         std::stable_sort(ho, ho + p->Bt, [hl](int32_t x, int32_t y) { return hl[x] > hl[y]; });
-        e = hipMemcpyAsync(lens_dev, hl, (size_t)p->Bt * 2 * sizeof(int32_t),
+        for (int64_t i = 0; i < p->Bt; ++i)
+            hs[i] = hl[ho[i]];
+        e = hipMemcpyAsync(lens_dev, hs, (size_t)p->Bt * 2 * sizeof(int32_t),
                            hipMemcpyHostToDevice, s);
         if (e != hipSuccess)
             return hip_fail(e, "sequence_lens copy");
@@ -271,6 +275,7 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
     ia.sbuf = p->phases == 2 ? (float *)(ws + p->ws.sbuf) : nullptr;
     ia.cbuf = p->op == RNN_OP_LSTM ? (float *)(ws + p->ws.cbuf) : nullptr;
     ia.lens_dev = lens_dev;
+    ia.order = order_dev;
     ia.fill_lens = sequence_lens ? -1 : (int32_t)p->S;
     ia.bar = (uint32_t *)(ws + p->ws.bar);
     ia.n_bar = n_flags(*p);
@@ -289,6 +294,7 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
     // directions in one launch), then its step loop
     const int64_t nchunks = (p->S + p->C - 1) / p->C;
     RecArgs ra = rec_args(*p, ws, B, P, Y, Y_h, Y_c);
+    ra.order = order_dev;
     for (int64_t ck = 0; ck < nchunks; ++ck) {
         const int64_t j0 = ck * p->C, j1 = std::min<int64_t>(p->S, j0 + p->C);
         if (ck == 0)
