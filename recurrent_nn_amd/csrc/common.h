@@ -42,8 +42,8 @@ struct Layout {
     size_t sbuf = 0;    // GRU lbr=0: r (.) H_prev of step j in plane j mod C, [C][D][Btp][Hp]
     size_t cbuf = 0;    // LSTM cell state between launches [D][Bt][H]
     size_t zbuf = 0;    // GRU lbr=0 update gate between launches [D][Bt][H]
-    size_t lens = 0;    // int32 [Bt]
-    size_t order = 0;   // int32 [Bt]: batch rows by decreasing sequence length
+    size_t lens = 0;    // int32 [2][Bt]: lengths by position, then the batch row at each
+                        // position (rows by decreasing length)
     size_t bar = 0;     // uint32 step flags [D*NBB][2][NUB], then int32 error word
     size_t cellb = 0;   // rnn_cell_run: summed biases expanded to [D][Wb = sum, Rb = 0]
     size_t total = 0;
@@ -159,8 +159,8 @@ struct ProjArgs {
     int64_t S, Bt, GH, D;
     int64_t steps;          // steps held by XW (the chunk length)
     int64_t j_base;         // first step of the chunk
-    const int32_t *lens;    // [Bt] on the device
-    const int32_t *order;   // [Bt] batch rows by decreasing length, or NULL (identity)
+    const int32_t *lens;    // [Bt] lengths by position, on the device
+    const int32_t *order;   // [Bt] batch row at each position (by decreasing length), or NULL
     int32_t reverse_only;   // direction 0 runs in reverse
     int32_t layout;         // 0: X [S][Bt][I]; 1: X [Bt][S][I]
     int32_t bf16;
