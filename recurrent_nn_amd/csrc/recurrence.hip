@@ -136,7 +136,7 @@ static size_t rec_shmem(const RecArgs &a)
     return a.halves == 2 ? rec_pipe_lds_bytes(a.BT, a.NT, a.U) : rec_lds_bytes(a.NW, a.BT, a.NT, a.U);
 }
 
-static int rec_threads(const RecArgs &a) { return a.exact ? 256 : 64 * a.NW; }
+static int rec_threads(const RecArgs &a) { return a.exact ? kExactThreads : 64 * a.NW; }
 
 int recurrence_can_persist(const RecArgs &a, int resident, int device, int *ok)
 {

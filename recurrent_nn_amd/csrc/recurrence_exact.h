@@ -28,6 +28,9 @@ namespace rnnamd {
 
 constexpr int kExactKT = 32;        // k values per staged chunk (Hp is a multiple)
 constexpr int kExactKTP = kExactKT + 4;   // LDS row stride (floats)
+// Threads per workgroup: eight waves, two per SIMD, so that one wave's LDS
+// and dependency waits are covered by the other's arithmetic.
+constexpr int kExactThreads = 512;
 
 // LDS bytes: H chunk [BT][KTP], R chunk [NTC][KTP], the sums [BT][NTC],
 // then h, c, z per pair, lengths, per-unit constants.
@@ -39,11 +42,12 @@ __host__ __device__ inline size_t rec_exact_lds_bytes(int bt, int nt, int u)
 }
 
 // Rows per thread for a block of bt rows and ntc columns (two columns per
-// thread): the rows per pass rpp = 256 / (ntc / 2), and ceil(bt / rpp)
+// thread, kExactThreads threads): the rows per pass rpp = kExactThreads /
+// (ntc / 2), and ceil(bt / rpp)
 // rounded up to a power of two.
 __host__ __device__ inline int rec_exact_nacc(int bt, int ntc)
 {
-    const int rpp = 256 / (ntc / 2);
+    const int rpp = kExactThreads / (ntc / 2);
     const int need = (bt + rpp - 1) / rpp;
     int n = 1;
     while (n < need)
@@ -52,7 +56,7 @@ __host__ __device__ inline int rec_exact_nacc(int bt, int ntc)
 }
 
 template <int NACC>
-__global__ void __launch_bounds__(256, 1) rec_exact_kernel(RecArgs a)
+__global__ void __launch_bounds__(kExactThreads, 1) rec_exact_kernel(RecArgs a)
 {
     constexpr int KT = kExactKT, KTP = kExactKTP;
     const int BT = a.BT;
@@ -100,7 +104,7 @@ __global__ void __launch_bounds__(256, 1) rec_exact_kernel(RecArgs a)
     // states at the start of this launch
     {
         const int j0 = a.q_begin / a.phases;
-        for (int pi = tid; pi < npairs; pi += 256) {
+        for (int pi = tid; pi < npairs; pi += kExactThreads) {
             const int rl = pi / uc, u = pi - rl * uc;
             const int s = row0 + rl;                      // position
             hst[pi] = a.hbuf[(size_t)(j0 % ring_n) * plane + drow + (size_t)rl * Hp + u0 + u];
@@ -109,9 +113,9 @@ __global__ void __launch_bounds__(256, 1) rec_exact_kernel(RecArgs a)
                           ? a.zbuf[((size_t)d * a.Bt + s) * a.H + u0 + u]
                           : 0.0f;
         }
-        for (int rl = tid; rl < rows; rl += 256)
+        for (int rl = tid; rl < rows; rl += kExactThreads)
             lst[rl] = a.lens[row0 + rl];
-        for (int e = tid; e < 11 * uc; e += 256) {
+        for (int e = tid; e < 11 * uc; e += kExactThreads) {
             const int k = e / uc, u = e - k * uc;
             float v = 0.0f;
             if (k < 4 && k < a.G && Wb)
@@ -127,14 +131,14 @@ __global__ void __launch_bounds__(256, 1) rec_exact_kernel(RecArgs a)
 
     // thread -> (columns c, c + NC2; rows r0 + rpp * i)
     const int NC2 = NTC / 2;
-    const int rpp = 256 / NC2;                   // rows per pass (NTC <= 128)
+    const int rpp = kExactThreads / NC2;         // rows per pass (NTC <= 128)
     const int c = tid % NC2;
     const int r0 = tid / NC2;
     const bool worker = r0 < rpp;
     // staging: H chunk = BT rows x KT/4 float4, R chunk = ncol rows x KT/4
     constexpr int Q = KT / 4;                    // float4 per row and chunk
-    constexpr int SH = 64 * Q / 256;             // H float4 per thread (BT <= 64)
-    constexpr int SR = 128 * Q / 256;            // R float4 per thread (ncol <= 128)
+    constexpr int SH = 64 * Q / kExactThreads;   // H float4 per thread (BT <= 64)
+    constexpr int SR = 128 * Q / kExactThreads;  // R float4 per thread (ncol <= 128)
     const int nchunks = Hp / KT;
 
     bool dead = false;
@@ -155,13 +159,13 @@ __global__ void __launch_bounds__(256, 1) rec_exact_kernel(RecArgs a)
             const int k0 = kc * KT;
 #pragma unroll
             for (int i = 0; i < SH; ++i) {
-                const int e = tid + 256 * i, rl = e / Q, kq = e - rl * Q;
+                const int e = tid + kExactThreads * i, rl = e / Q, kq = e - rl * Q;
                 if (rl < BT)
                     hreg[i] = *(const f4 *)(asrc + (size_t)rl * Hp + k0 + 4 * kq);
             }
 #pragma unroll
             for (int i = 0; i < SR; ++i) {
-                const int e = tid + 256 * i, cl = e / Q, kq = e - cl * Q;
+                const int e = tid + kExactThreads * i, cl = e / Q, kq = e - cl * Q;
                 if (cl < ncol)
                     rreg[i] = *(const f4 *)(rsrc + (size_t)cl * Hp + k0 + 4 * kq);
             }
@@ -169,13 +173,13 @@ __global__ void __launch_bounds__(256, 1) rec_exact_kernel(RecArgs a)
         auto sstore = [&]() {
 #pragma unroll
             for (int i = 0; i < SH; ++i) {
-                const int e = tid + 256 * i, rl = e / Q, kq = e - rl * Q;
+                const int e = tid + kExactThreads * i, rl = e / Q, kq = e - rl * Q;
                 if (rl < BT)
                     *(f4 *)(hs + rl * KTP + 4 * kq) = hreg[i];
             }
 #pragma unroll
             for (int i = 0; i < SR; ++i) {
-                const int e = tid + 256 * i, cl = e / Q, kq = e - cl * Q;
+                const int e = tid + kExactThreads * i, cl = e / Q, kq = e - cl * Q;
                 if (cl < ncol)
                     *(f4 *)(rs + cl * KTP + 4 * kq) = rreg[i];
             }
@@ -230,7 +234,7 @@ __global__ void __launch_bounds__(256, 1) rec_exact_kernel(RecArgs a)
         // ---- gate arithmetic of each (row, unit) pair, in the written order
         float *hnext = a.hbuf + (size_t)((j + 1) % ring_n) * plane + drow;
         float *snext = a.sbuf ? a.sbuf + (size_t)(j % a.xw_steps) * plane + drow : nullptr;
-        for (int pi = tid; pi < npairs; pi += 256) {
+        for (int pi = tid; pi < npairs; pi += kExactThreads) {
             const int rl = pi / uc, u = pi - rl * uc;
             const int s = row0 + rl;                      // position (XW row)
             const int b = a.order ? a.order[s] : s;       // batch row (outputs)
@@ -281,7 +285,7 @@ __global__ void __launch_bounds__(256, 1) rec_exact_kernel(RecArgs a)
         if (u0 + uc == a.H && Hp > a.H && (last_phase || a.phases == 2)) {
             float *pl = last_phase ? hnext : snext;
             const int padw = Hp - a.H;
-            for (int e = tid; e < rows * padw; e += 256)
+            for (int e = tid; e < rows * padw; e += kExactThreads)
                 store_coherent(pl + (size_t)(e / padw) * Hp + a.H + e % padw, 0.0f);
         }
         if (q + 1 < a.q_end)
@@ -293,7 +297,7 @@ __global__ void __launch_bounds__(256, 1) rec_exact_kernel(RecArgs a)
 
     // ---- end of this launch: keep or publish the states ---------------------
     const bool done = a.q_end == a.S * a.phases;
-    for (int pi = tid; pi < npairs; pi += 256) {
+    for (int pi = tid; pi < npairs; pi += kExactThreads) {
         const int rl = pi / uc, u = pi - rl * uc;
         const int s = row0 + rl;
         const int b = a.order ? a.order[s] : s;           // batch row (outputs)
