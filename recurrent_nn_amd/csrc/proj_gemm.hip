@@ -361,13 +361,16 @@ __global__ void __launch_bounds__(256, 3) proj_gemm_kernel(ProjArgs a)
 // and add rounded on its own (for bf16 the operands are the rounded bf16
 // values, whose products are exact in binary32).  VALU only; the value does
 // not depend on the tiling.  64x64 tile per 256-thread workgroup, each
-// thread 4x4 outputs (rows ty + 16 i, columns tx + 16 j), k staged through
-// LDS in chunks of 32.  Same rows, tile skip and XW order as the fast form.
+// thread 4x4 outputs (rows 4 ty .. 4 ty + 3, columns 4 tx .. 4 tx + 3, so
+// that a k step reads each operand with one 16-byte LDS load); k staged
+// through LDS in chunks of 32, k-major, the next chunk loaded into registers
+// while the current one is consumed.  Same rows, tile skip and XW order as
+// the fast form.
 template <bool BF16>
 __global__ void __launch_bounds__(256) proj_exact_kernel(ProjArgs a)
 {
-    constexpr int TM = 64, TN = 64, KC = 32;
-    __shared__ float As[KC][TM + 1], Bs[KC][TN + 1];
+    constexpr int TM = 64, TN = 64, KC = 32, LDT = TM + 4;
+    __shared__ __attribute__((aligned(16))) float As[KC][LDT], Bs[KC][LDT];
     __shared__ int64_t xrow_s[TM];
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const int64_t Md = a.steps * a.Bt;
@@ -385,7 +388,63 @@ __global__ void __launch_bounds__(256) proj_exact_kernel(ProjArgs a)
     const float *X = (const float *)a.X;
     const uint16_t *Xb = BF16 ? a.Xb + (size_t)d * Md * a.K : nullptr;
     const char *Wd = (const char *)a.Wp + (size_t)d * a.GH * a.K * (BF16 ? 2 : 4);
-    auto bf = [](uint16_t h) { return __uint_as_float((uint32_t)h << 16); };
+    auto bf = [](uint32_t h) { return __uint_as_float(h << 16); };
+
+    // staging: thread -> (row r = tid / 8 + 32 i, 4 k at 4 (tid % 8)), i < 2
+    const int sr = tid >> 3, sk = (tid & 7) * 4;
+    auto row_a = [&](int r) -> int64_t {        // source row of A, or -1
+        if (BF16)
+            return m0 + r < Md ? m0 + r : -1;
+        return xrow_s[r];
+    };
+    auto row_b = [&](int r) -> int64_t { return n0 + r < a.GH ? n0 + r : -1; };
+    // four consecutive k of a row (zeros past K or for a missing row)
+    auto load4k = [&](bool is_b, int64_t row, int64_t k) -> f4 {
+        f4 v = {0.f, 0.f, 0.f, 0.f};
+        if (row < 0)
+            return v;
+        if (BF16) {
+            const uint16_t *src = is_b ? (const uint16_t *)Wd : Xb;
+            const uint16_t *q = src + (size_t)row * a.K + k;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (k + e < a.K)
+                    v[e] = bf(q[e]);
+        } else {
+            const float *src = is_b ? (const float *)Wd : X;
+            const float *q = src + (size_t)row * a.K + k;
+            if (a.K % 4 == 0 && k + 3 < a.K)
+                return *(const f4 *)q;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (k + e < a.K)
+                    v[e] = q[e];
+        }
+        return v;
+    };
+    int64_t ra_[2], rb_[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        ra_[i] = row_a(sr + 32 * i);
+        rb_[i] = row_b(sr + 32 * i);
+    }
+    f4 ga[2], gb[2];
+    auto gload = [&](int64_t k0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            ga[i] = load4k(false, ra_[i], k0 + sk);
+            gb[i] = load4k(true, rb_[i], k0 + sk);
+        }
+    };
+    auto sstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                As[sk + e][sr + 32 * i] = ga[i][e];
+                Bs[sk + e][sr + 32 * i] = gb[i][e];
+            }
+    };
 
     float acc[4][4];
 #pragma unroll
@@ -393,54 +452,34 @@ __global__ void __launch_bounds__(256) proj_exact_kernel(ProjArgs a)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             acc[i][j] = 0.0f;
+    gload(0);
     for (int64_t k0 = 0; k0 < a.K; k0 += KC) {
         const int kn = (int)(a.K - k0 < KC ? a.K - k0 : KC);
-        for (int e = tid; e < TM * KC; e += 256) {
-            const int r = e / KC, kk = e - r * KC;
-            const int64_t k = k0 + kk;
-            float va = 0.0f, vb = 0.0f;
-            if (kk < kn) {
-                if (BF16) {
-                    if (m0 + r < Md)
-                        va = bf(Xb[(size_t)(m0 + r) * a.K + k]);
-                    if (n0 + r < a.GH)
-                        vb = bf(((const uint16_t *)Wd)[(size_t)(n0 + r) * a.K + k]);
-                } else {
-                    if (xrow_s[r] >= 0)
-                        va = X[(size_t)xrow_s[r] * a.K + k];
-                    if (n0 + r < a.GH)
-                        vb = ((const float *)Wd)[(size_t)(n0 + r) * a.K + k];
-                }
-            }
-            As[kk][r] = va;
-            Bs[kk][r] = vb;
-        }
+        __syncthreads();                         // the previous chunk is consumed
+        sstore();
         __syncthreads();
+        if (k0 + KC < a.K)
+            gload(k0 + KC);
         for (int kk = 0; kk < kn; ++kk) {
-            float av[4], bv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                av[i] = As[kk][ty + 16 * i];
-                bv[i] = Bs[kk][tx + 16 * i];
-            }
+            const f4 av = *(const f4 *)&As[kk][4 * ty];
+            const f4 bv = *(const f4 *)&Bs[kk][4 * tx];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __fadd_rn(acc[i][j], __fmul_rn(av[i], bv[j]));
         }
-        __syncthreads();
     }
     float *XWd = a.XW + (size_t)d * Md * a.GH;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + ty + 16 * i;
+        const int64_t m = m0 + 4 * ty + i;
         if (m >= Md)
             continue;
         const size_t ro = (size_t)m * a.GH;     // step j - j_base, position i
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t n = n0 + tx + 16 * j;
+            const int64_t n = n0 + 4 * tx + j;
             if (n < a.GH)
                 XWd[ro + n] = acc[i][j];
         }
