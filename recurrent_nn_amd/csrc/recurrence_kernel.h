@@ -322,7 +322,7 @@ __device__ __forceinline__ float gru0_candidate(float xh, float rh, const float 
 // states (h, c, z) and the per-row lengths.
 __host__ __device__ inline size_t rec_lds_bytes(int nw, int bt, int nt, int u)
 {
-    return ((size_t)nw * bt * (nt * 16 + 4) + 3 * (size_t)bt * u + bt + 11 * (size_t)u) * 4;
+    return ((size_t)nw * bt * (nt * 16 + 4) + 3 * (size_t)bt * u + 2 * bt + 11 * (size_t)u) * 4;
 }
 
 // Depth (in 16-k blocks) of the A-operand prefetch of the register-resident
@@ -338,13 +338,15 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
     constexpr int BT = MT * 16;
     constexpr int NTC = NT * 16;
     constexpr int LDR = NTC + 4;                 // LDS row stride of the partial tiles
+    constexpr int PH = TA > 0 ? 2 : 1;           // phases per step (2: GRU, linear_before_reset 0)
     extern __shared__ float smem[];
     float *red = smem;                           // [kWaves][BT][LDR] partial tiles
     float *hst = red + kWaves * BT * LDR;        // [BT * U] h of each (row, unit) pair
     float *cst = hst + BT * a.U;                 // [BT * U] LSTM cell state
     float *zst = cst + BT * a.U;                 // [BT * U] GRU update gate between phases
     int *lst = (int *)(zst + BT * a.U);          // [BT] sequence length of each row
-    float *cst_u = (float *)(lst + BT);          // [11][U] Wb, Rb per gate, then Pi, Po, Pf
+    int *ost = lst + BT;                         // [BT] batch row held at each position
+    float *cst_u = (float *)(ost + BT);          // [11][U] Wb, Rb per gate, then Pi, Po, Pf
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -365,11 +367,12 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
     const int KB = RES ? KBR : a.KB;
     const int Hp = a.Hp;
     const bool rev = a.reverse_only || d == 1;
-    const int GH = a.G * a.H;
     // ACT fixes the operator too: 1 LSTM, 2 and 4 GRU, 3 RNN; 0 reads it at run time
     const int op = ACT == 1 ? (int)RNN_OP_LSTM
                  : (ACT == 2 || ACT == 4) ? (int)RNN_OP_GRU
                  : ACT == 3 ? (int)RNN_OP_RNN : a.op;
+    const int G = ACT == 1 ? 4 : (ACT == 2 || ACT == 4) ? 3 : ACT == 3 ? 1 : a.G;   // gates
+    const int GH = G * a.H;
     const size_t plane = (size_t)a.D * a.Btp * Hp;           // one plane of the H history
     const size_t drow = ((size_t)d * a.Btp + row0) * Hp;     // this group's rows
     const int grp = d * a.NBB + bb;
@@ -378,7 +381,7 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
     const float *Wb = a.B ? a.B + (size_t)d * 2 * GH : nullptr;
     const float *Rb = a.B ? Wb + GH : nullptr;
     const float *Pd = a.P ? a.P + (size_t)d * 3 * a.H : nullptr;
-    const size_t xwd = (size_t)d * a.xw_steps * a.Bt * GH + (size_t)ub * a.G * a.U;
+    const size_t xwd = (size_t)d * a.xw_steps * a.Bt * GH + (size_t)ub * G * a.U;
     const int npairs = rows * uc;
 
     // R fragments: lane (lr, lq) of wave w holds R[col nt*16 + lr][k] for
@@ -395,27 +398,29 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
 
     // states at the start of this launch
     {
-        const int j0 = a.q_begin / a.phases;
+        const int j0 = a.q_begin / PH;
         for (int pi = tid; pi < npairs; pi += kThreads) {
             const int rl = pi / uc, u = pi - rl * uc;
             const int s = row0 + rl;                      // position
             hst[pi] = a.hbuf[(size_t)(j0 % (a.xw_steps + 1)) * plane + drow + (size_t)rl * Hp + u0 + u];
             cst[pi] = op == RNN_OP_LSTM ? a.cbuf[((size_t)d * a.Bt + s) * a.H + u0 + u] : 0.0f;
-            zst[pi] = (a.phases == 2 && (a.q_begin % 2) == 1)
+            zst[pi] = (PH == 2 && (a.q_begin % 2) == 1)
                           ? a.zbuf[((size_t)d * a.Bt + s) * a.H + u0 + u]
                           : 0.0f;
         }
-        for (int rl = tid; rl < rows; rl += kThreads)
+        for (int rl = tid; rl < rows; rl += kThreads) {
             lst[rl] = a.lens[row0 + rl];
+            ost[rl] = a.order ? a.order[row0 + rl] : row0 + rl;
+        }
         // Wb, Rb (zeros when B is absent: adding +0 to a pre-activation is the
         // identity here, since xw + rec is never -0 -- both sums start at +0),
         // then the peepholes Pi, Po, Pf
         for (int e = tid; e < 11 * uc; e += kThreads) {
             const int k = e / uc, u = e - k * uc;
             float v = 0.0f;
-            if (k < 4 && k < a.G && Wb)
+            if (k < 4 && k < G && Wb)
                 v = Wb[k * a.H + u0 + u];
-            else if (k >= 4 && k < 8 && k - 4 < a.G && Rb)
+            else if (k >= 4 && k < 8 && k - 4 < G && Rb)
                 v = Rb[(k - 4) * a.H + u0 + u];
             else if (k >= 8 && Pd)
                 v = Pd[(k - 8) * a.H + u0 + u];
@@ -424,80 +429,55 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
         __syncthreads();
     }
 
-    constexpr bool kPrefetchXW = P <= 2;
-    float xw_next[kPrefetchXW ? P : 1][4];
-    if constexpr (kPrefetchXW) {
+    // XW of pair pi for phase qq (zeros for an absent pair or a row no longer
+    // active).  XW is stored by step: row (jj - j_base, position) already
+    // holds the projection of the time index this step reads (reverse
+    // included).
+    auto fetch_xw_q = [&](int qq, int pi, float *xv) {
 #pragma unroll
-        for (int i = 0; i < P; ++i) {
-            const int pi = tid + kThreads * i;
+        for (int g = 0; g < 4; ++g)
+            xv[g] = 0.0f;
+        const int jj = qq / PH, pp = qq - jj * PH;
+        const int rl = pi / uc, u = pi - rl * uc;
+        if (pi >= npairs || jj >= lst[rl])
+            return;
+        const float *src = a.XW + xwd + ((size_t)(jj - a.j_base) * a.Bt + row0 + rl) * GH + u;
 #pragma unroll
+        for (int g = 0; g < 4; ++g)
+            if (g < G && (PH == 1 || (pp == 1) == (g == 2)))
+                xv[g] = src[g * uc];
+    };
+    // Each phase's XW values are loaded during the previous phase's product
+    // (issued after its last H load, so that no product wait is held up by
+    // them), the first phase's before the loop.
+    float xw_next[P][4];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        if (a.q_begin < a.q_end)
+            fetch_xw_q(a.q_begin, tid + kThreads * i, xw_next[i]);
+        else
             for (int g = 0; g < 4; ++g)
                 xw_next[i][g] = 0.0f;
-            if (pi < npairs && a.q_begin < a.q_end) {
-                const int jj = a.q_begin / a.phases, pp = a.q_begin - jj * a.phases;
-                const int rl = pi / uc, u = pi - rl * uc;
-                const int len = lst[rl];
-                if (jj < len) {
-                    const float *src =
-                        a.XW + xwd + ((size_t)(jj - a.j_base) * a.Bt + row0 + rl) * GH + u;
-#pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        if (g < a.G && ((a.phases == 2 && pp == 1) ? g == 2 : !(a.phases == 2 && g == 2)))
-                            xw_next[i][g] = src[g * uc];
-                }
-            }
-        }
     }
     bool dead = false;
     for (int q = a.q_begin; q < a.q_end; ++q) {
-        const int j = q / a.phases;
-        const int ph = q - j * a.phases;
+        const int j = q / PH;
+        const int ph = q - j * PH;
         const int t0 = ph == 0 ? 0 : a.NTA;              // this phase's column tiles
         const int t1 = ph == 0 ? a.NTA : a.NTA + a.NTB;
-        const bool last_phase = ph == a.phases - 1;
+        const bool last_phase = ph == PH - 1;
 
-        // XW of pair pi for phase qq (0 for inactive rows)
-        auto fetch_xw_q = [&](int qq, int pi, float *xv) {
-            xv[0] = xv[1] = xv[2] = xv[3] = 0.0f;
-            const int jj = qq / a.phases, pp = qq - jj * a.phases;
-            const int rl = pi / uc, u = pi - rl * uc;
-            const int len = lst[rl];
-            if (jj >= len)
-                return;
-            // XW is stored by step: row (jj - j_base, b) already holds the
-            // projection of the time index this step reads (reverse included)
-            const float *src = a.XW + xwd + ((size_t)(jj - a.j_base) * a.Bt + row0 + rl) * GH + u;
-            if (a.phases == 2 && pp == 1) {
-                xv[2] = src[2 * uc];
-            } else {
+        float xw[P][4];
 #pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    if (g < a.G && !(a.phases == 2 && g == 2))
-                        xv[g] = src[g * uc];
-            }
-        };
-        auto fetch_xw = [&](int pi, float *xv) { fetch_xw_q(q, pi, xv); };
-        // With few pairs per thread the XW values of the NEXT phase are loaded
-        // during this one (issued after the product's last H load, so no
-        // product wait is held up by them); this phase uses last phase's.
-        float xw[kPrefetchXW ? P : 1][4];
-        if constexpr (kPrefetchXW) {
+        for (int i = 0; i < P; ++i)
 #pragma unroll
-            for (int i = 0; i < P; ++i)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    xw[i][g] = xw_next[i][g];
-        }
+            for (int g = 0; g < 4; ++g)
+                xw[i][g] = xw_next[i][g];
         auto prefetch_xw = [&]() {
-            if constexpr (kPrefetchXW) {
-                if (q + 1 < a.q_end) {
+            if (q + 1 < a.q_end) {
 #pragma unroll
-                    for (int i = 0; i < P; ++i) {
-                        const int pi = tid + kThreads * i;
-                        if (pi < npairs)
-                            fetch_xw_q(q + 1, pi, xw_next[i]);
-                    }
-                }
+                for (int i = 0; i < P; ++i)
+                    fetch_xw_q(q + 1, tid + kThreads * i, xw_next[i]);
             }
         };
 
@@ -558,14 +538,14 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
         float *snext = a.sbuf ? a.sbuf + (size_t)(j % a.xw_steps) * plane + drow : nullptr;
         auto do_pair = [&](int pi, const float *xv, auto F, auto Gf, auto Hf) {
             const int rl = pi / uc, u = pi - rl * uc;
-            const int b = a.order ? a.order[row0 + rl] : row0 + rl;   // batch row (outputs)
+            const int b = ost[rl];                         // batch row (outputs)
             const int gu = u0 + u;                         // hidden unit
             const int len = lst[rl];
             const bool active = j < len;
             const float hp = hst[pi];
             float hn = hp, cn = cst[pi];
             if (active) {
-                if (op != RNN_OP_GRU || a.phases == 1) {    // (compile-time for LSTM, RNN)
+                if (op != RNN_OP_GRU || PH == 1) {    // (compile-time for LSTM, RNN)
                     hn = gates_one_phase(
                         op, xv, [&](int g) { return rec_at(rl, g * uc + u); },
                         [&](int e) { return cst_u[e * a.U + u]; }, Pd != nullptr, a.clip_on, a.clip, a.input_forget != 0, hp, cn, F, Gf, Hf);
@@ -578,7 +558,7 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
                     hn = gru0_candidate(xv[2], rec_at(rl, a.NTA * 16 + u), cst_u, a.U, u,
                                         a.clip_on, a.clip, zst[pi], hp, Gf);
                 }
-            } else if (a.phases == 2 && ph == 0) {
+            } else if (PH == 2 && ph == 0) {
                 store_coherent(snext + (size_t)rl * Hp + gu, 0.0f);
             }
             if (last_phase) {
@@ -595,21 +575,30 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
             }
         };
 
+        // (up to 8 pairs: one pair per iteration, not unrolled, since the
+        // unrolled form ran out of registers; the pair's XW values are moved
+        // down the array instead of indexed at run time)
         auto run_pairs = [&](auto F, auto Gf, auto Hf) {
-            if constexpr (kPrefetchXW) {
+            if constexpr (P <= 2) {
 #pragma unroll
                 for (int i = 0; i < P; ++i) {
                     const int pi = tid + kThreads * i;
                     if (pi < npairs)
                         do_pair(pi, xw[i], F, Gf, Hf);
                 }
-            } else {
+                return;
+            }
 #pragma unroll 1
-                for (int pi = tid; pi < npairs; pi += kThreads) {
-                    float xv[4];
-                    fetch_xw(pi, xv);
-                    do_pair(pi, xv, F, Gf, Hf);
-                }
+            for (int i = 0; i < P; ++i) {
+                const int pi = tid + kThreads * i;
+                if (pi >= npairs)
+                    break;
+                do_pair(pi, xw[0], F, Gf, Hf);
+#pragma unroll
+                for (int k = 0; k + 1 < P; ++k)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        xw[k][g] = xw[k + 1][g];
             }
         };
         // ACT (compile time): 1 LSTM Sigmoid/Tanh/Tanh, 2 GRU HardSigmoid/Tanh,
@@ -624,7 +613,7 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
             run_pairs(ActAny{fa}, ActAny{ga}, ActAny{ha});
         // The last unit block also writes the padding columns [H, Hp) of the
         // plane it published, as zeros (they meet zero rows of R).
-        if (u0 + uc == a.H && Hp > a.H && (last_phase || a.phases == 2)) {
+        if (u0 + uc == a.H && Hp > a.H && (last_phase || PH == 2)) {
             float *pl = last_phase ? hnext : snext;
             const int padw = Hp - a.H;
             for (int e = tid; e < rows * padw; e += kThreads)
@@ -638,15 +627,15 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
     }
 
     // ---- end of this launch: keep or publish the states ---------------------
-    const bool done = a.q_end == a.S * a.phases;
+    const bool done = a.q_end == a.S * PH;
     for (int pi = tid; pi < npairs; pi += kThreads) {
         const int rl = pi / uc, u = pi - rl * uc;
         const int s = row0 + rl;
-        const int b = a.order ? a.order[s] : s;           // batch row (outputs)
+        const int b = ost[rl];                            // batch row (outputs)
         const size_t so = ((size_t)d * a.Bt + s) * a.H + u0 + u;
         if (op == RNN_OP_LSTM)
             a.cbuf[so] = cst[pi];
-        if (a.phases == 2)
+        if (PH == 2)
             a.zbuf[so] = zst[pi];
         if (done) {
             const size_t yo = a.layout == 0 ? ((size_t)d * a.Bt + b) * a.H + u0 + u
