@@ -319,6 +319,9 @@ __global__ void __launch_bounds__(256, 3) proj_gemm_kernel(ProjArgs a)
     __syncthreads();
     for (int kt = 0; kt + 1 < nkf; ++kt) {
         gload_fast(kt + 1, ra, rb);
+        // left to itself the scheduler sinks these loads to just before
+        // their LDS stores, exposing their whole latency
+        __builtin_amdgcn_sched_barrier(0);
         stage(0);
         __syncthreads();
         sstore(0, ra, rb);
