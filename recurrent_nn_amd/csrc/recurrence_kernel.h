@@ -56,6 +56,55 @@ __device__ __forceinline__ void store_coherent(float *p, float v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Wait until flags[0 .. n) all reach `target` (one wave; every lane reads a
+// share of the flags).  More than spin_limit polls raises the error word and
+// stops waiting.
+__device__ __forceinline__ void wave_wait_flags(const uint32_t *flags, int n, uint32_t target,
+                                                int32_t *err, uint32_t spin_limit, bool &dead)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t polls = 0;
+    for (;;) {
+        bool ok = true;
+        for (int i = lane; i < n; i += 64)
+            ok = ok && __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target;
+        if (__all(ok))
+            break;
+        __builtin_amdgcn_s_sleep(1);
+        if (++polls > spin_limit) {
+            if (lane == 0)
+                __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            dead = true;
+            break;
+        }
+    }
+    asm volatile("" ::: "memory");   // no later load is moved above the wait
+}
+
+// First and last H column of the 64-column (256-byte) spans that hold the
+// columns [k0, k1) of a plane row (rows start 256-byte aligned: Hp is a
+// multiple of 64).
+__device__ __forceinline__ int kline_lo(int k0) { return k0 & ~63; }
+__device__ __forceinline__ int kline_hi(int k1, int Hp) { return min(Hp, (k1 + 63) & ~63) - 1; }
+
+// Step hand-over among the NUB workgroups of one (direction, batch block)
+// group when the waves split k: the workgroup publishes "phase q done" in its
+// own flag once every wave's coherent stores have completed (the barrier
+// also ends this phase's reads of the partial tiles), then each wave waits
+// only for the flags of the unit blocks [lo, lo + n) that write the cache
+// lines its own k range reads.
+__device__ __forceinline__ void group_publish_wait(uint32_t *flags, int me, uint32_t target, int lo,
+                                                   int n, int32_t *err, uint32_t spin_limit,
+                                                   bool withhold, bool &dead)
+{
+    wait_stores();                 // this wave's coherent stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0 && !withhold)
+        __hip_atomic_store(flags + me, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!dead)
+        wave_wait_flags(flags + lo, n, target, err, spin_limit, dead);
+}
+
 // Step barrier among the NUB workgroups of one (direction, batch block)
 // group: each workgroup publishes "phase q done" in its own flag after its
 // coherent stores have completed, then one wave polls the group's flags.
@@ -384,6 +433,14 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
     const size_t xwd = (size_t)d * a.xw_steps * a.Bt * GH + (size_t)ub * G * a.U;
     const int npairs = rows * uc;
 
+    // The unit blocks whose H columns this wave's k range reads (the columns
+    // [H, Hp) are written by the last unit block), widened to whole 64-column
+    // (256-byte) spans: a load brings in its whole cache line, and a line
+    // that also holds columns of a unit block not yet waited for would stay
+    // stale in this CU's and XCD's caches for the waves that read them next.
+    const int wub_lo = min(kline_lo(w * KB * 16) / a.U, a.NUB - 1);
+    const int wub_hi = min(a.NUB - 1, kline_hi((w + 1) * KB * 16, Hp) / a.U);
+
     // R fragments: lane (lr, lq) of wave w holds R[col nt*16 + lr][k] for
     // k = w*KB*16 + kb*16 + 4*lq + s, s = 0..3.
     const float *rfrag = a.Rp + ((size_t)(d * a.NUB + ub) * NTC + lr) * Hp + w * KB * 16 + 4 * lq;
@@ -620,8 +677,9 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
                 store_coherent(pl + (size_t)(e / padw) * Hp + a.H + e % padw, 0.0f);
         }
         if (q + 1 < a.q_end)
-            group_barrier(a.bar + (size_t)grp * 2 * a.NUB, a.NUB, ub, (uint32_t)(q + 1), a.err,
-                          a.spin_limit, a.withhold_flags != 0, dead);
+            group_publish_wait(a.bar + (size_t)grp * 2 * a.NUB, ub, (uint32_t)(q + 1), wub_lo,
+                               wub_hi - wub_lo + 1, a.err, a.spin_limit, a.withhold_flags != 0,
+                               dead);
         else
             __syncthreads();
     }

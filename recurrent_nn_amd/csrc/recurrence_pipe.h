@@ -26,31 +26,6 @@
 
 namespace rnnamd {
 
-// Wait until flags[0 .. n) all reach `target` (one wave; every lane reads a
-// share of the flags).  More than spin_limit polls raises the error word and
-// stops waiting.
-__device__ __forceinline__ void wave_wait_flags(const uint32_t *flags, int n, uint32_t target,
-                                                int32_t *err, uint32_t spin_limit, bool &dead)
-{
-    const int lane = threadIdx.x & 63;
-    uint32_t polls = 0;
-    for (;;) {
-        bool ok = true;
-        for (int i = lane; i < n; i += 64)
-            ok = ok && __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target;
-        if (__all(ok))
-            break;
-        __builtin_amdgcn_s_sleep(1);
-        if (++polls > spin_limit) {
-            if (lane == 0)
-                __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            dead = true;
-            break;
-        }
-    }
-    asm volatile("" ::: "memory");   // no later load is moved above the wait
-}
-
 // The register-resident product (as product_res) with A tiles prefetched PD
 // k blocks ahead.  The first PD blocks are loaded by prime_ring beforehand
 // (so that their latency overlaps other work); `mid` runs right after the
@@ -189,10 +164,11 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
     const int npairs = rows * uc;
 
     // The unit blocks whose H columns this wave's k range reads (the columns
-    // [H, Hp) are written by the last unit block).
+    // [H, Hp) are written by the last unit block), widened to whole cache
+    // lines as in the four-wave kernel (a no-op here: KBR * 16 >= 128).
     const int k0 = w * KBR * 16;
-    const int wub_lo = min(k0 / a.U, a.NUB - 1);
-    const int wub_hi = min(a.NUB - 1, (k0 + KBR * 16 - 1) / a.U);
+    const int wub_lo = min(kline_lo(k0) / a.U, a.NUB - 1);
+    const int wub_hi = min(a.NUB - 1, kline_hi(k0 + KBR * 16, Hp) / a.U);
 
     // R fragments, as in the four-wave kernel
     const float *rfrag = a.Rp + ((size_t)(d * a.NUB + ub) * NTC + lr) * Hp + k0 + 4 * lq;
