@@ -289,6 +289,16 @@ def main():
     stage_ms = {k: float(np.mean(v)) for k, v in per.items()}
     print(f"[bench] stage ms: {json.dumps(stage_ms)}", file=sys.stderr, flush=True)
 
+    # ---- each invocation timed on its own, for the median and the minimum ----
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a_, b_ in evs:
+        a_.record(stream)
+        step()
+        b_.record(stream)
+    torch.cuda.synchronize()
+    each = sorted(a_.elapsed_time(b_) for a_, b_ in evs)
+
     proj_f, rec_f = flops_per_run(c)
     proj_peak = BF16_MFMA_PEAK_TFLOPS if c.proj_bf16 else FP32_MFMA_PEAK_TFLOPS
     bound = "mfma"
@@ -308,6 +318,15 @@ def main():
     }
     for k in kernels.values():
         k["frac"] = k["achieved"] / k["peak"]
+    # the recurrence's operand streams per step: R (what a kernel that streamed
+    # it would need, against HBM) and the H rows every workgroup reads (L2)
+    desc = dict(kv.split("=", 1) for kv in plan.describe().split() if "=" in kv)
+    t_step = stage_ms["recurrence"] * 1e-3 / c.seq
+    r_bytes = 4.0 * c.dirs * c.gates * c.hidden * c.hidden
+    h_bytes = 4.0 * int(desc["workgroups"]) * int(desc["BT"]) * int(desc["Hp"])
+    kernels["recurrence"]["r_stream_gbs"] = r_bytes / t_step / 1e9
+    kernels["recurrence"]["r_stream_frac_hbm"] = r_bytes / t_step / (HBM_PEAK_GBS * 1e9)
+    kernels["recurrence"]["h_broadcast_gbs"] = h_bytes / t_step / 1e9
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
     dk = kernels[dom]
     roofline = {"bound": dk["bound"], "achieved": round(dk["achieved"], 3), "peak": dk["peak"],
@@ -328,6 +347,8 @@ def main():
                    "layout": c.layout, "global_batch": c.batch, "seq_len": c.seq,
                    "parallelism": "none (1 GPU)", "plan": plan.describe()},
         "valid_cell_updates_per_s": c.valid_cell_updates() / (ms * 1e-3),
+        "ms_per_step_median": each[len(each) // 2], "ms_per_step_min": each[0],
+        "inputs_sha256": c.digests(),
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                         for kk, vv in v.items()} for k, v in kernels.items()},
@@ -337,6 +358,7 @@ def main():
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cb = cpu_baseline(c, args.cpu_budget_s)
         res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        res["gpu_over_cpu_baseline"] = value / cb["value"]
     print(json.dumps(res), flush=True)
 
 
