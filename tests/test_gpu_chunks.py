@@ -39,7 +39,9 @@ CASES = [
     # bidirectional LSTM, peepholes, the pipelined kernel (hidden 512)
     dict(op="LSTM", direction="bidirectional", S=17, Bt=40, I=32, H=512, with_lens=True,
          with_p=True, chunks=[4, 6]),
-    # GRU with two phases per step
+    # GRU with two phases per step; 16 columns of H per wave, so that a wave's
+    # k range is part of a cache line that other unit blocks also write (the
+    # step hand-over must wait for all of them)
     dict(op="GRU", direction="bidirectional", S=13, Bt=20, I=16, H=64, with_lens=True,
          linear_before_reset=0, chunks=[2, 5]),
     # RNN, full lengths, layout 1
