@@ -48,6 +48,8 @@ def parse():
                    help="exact mode: k-ordered unfused products on the VALU (results bit-identical "
                         "to the oracle); reported against the fp32 vector peak")
     p.add_argument("--time-chunk", type=int, default=0, help="steps per time chunk (0: all)")
+    p.add_argument("--peaks", action="store_true",
+                   help="print library references (HBM copy, fp32/bf16 GEMM) and exit")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB -> 1 GiB device copy kernel (to scale HBM counters)")
     p.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -93,6 +95,45 @@ def copy_calibration():
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES}), flush=True)
+
+
+def achievable_peaks():
+    """Library references on this part, next to the spec peaks: a plain 1 GiB
+    device-to-device copy (HBM read + write), and torch's own fp32 and bf16
+    matrix products at the plain shapes of the fp32 (S 512, Bt 64, I 1024,
+    G*H*D 8192) and bf16 (S 256, Bt 256, I 2048, G*H 6144) projections, with
+    no row gather.  Context only: nothing on the measured path uses them."""
+    import torch
+    dev = torch.device("cuda:0")
+
+    def ms_per(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    copy_ms = ms_per(lambda: dst.copy_(src), 10)
+    del src, dst
+    out = {"hbm_copy_gbs": 2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9}
+    for name, (M, N, K, dt) in {"fp32_gemm_tflops": (32768, 8192, 1024, torch.float32),
+                                "bf16_gemm_tflops": (65536, 6144, 2048, torch.bfloat16)}.items():
+        g = torch.Generator(device=dev).manual_seed(0)
+        a = torch.randn(M, K, device=dev, generator=g).to(dt)
+        b = torch.randn(K, N, device=dev, generator=g).to(dt)      # [K, N], contiguous
+        ms = ms_per(lambda: torch.matmul(a, b), 5)
+        out[name] = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        del a, b
+    out["spec"] = {"hbm_gbs": HBM_PEAK_GBS, "fp32_mfma_tflops": FP32_MFMA_PEAK_TFLOPS,
+                   "bf16_mfma_tflops": BF16_MFMA_PEAK_TFLOPS}
+    print(json.dumps(out), flush=True)
 
 
 def _pmc_rows(d, counter=False):
@@ -236,6 +277,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.peaks:
+        achievable_peaks()
         return
     ra._lib.load()
     dev = torch.device("cuda:0")
