@@ -235,6 +235,36 @@ def test_feature_cases_match_oracle(k):
     compare(c, run_gpu(c))
 
 
+# The streamed kernel with up to 8 (row, unit) pairs per thread, forced
+# through units_per_block: XW of every pair is loaded during the previous
+# product, for one phase (GRU linear_before_reset = 0: z and r, then the
+# candidate) or both; ragged batch blocks leave threads with fewer pairs.
+EIGHT_PAIRS = [
+    (dict(op="GRU", direction="bidirectional", S=5, Bt=70, I=16, H=64, with_lens=True,
+          linear_before_reset=0), 16),                  # 4 pairs per thread, two phases
+    (dict(op="GRU", direction="bidirectional", S=4, Bt=37, I=12, H=96, with_lens=True,
+          linear_before_reset=0, clip=0.9), 32),        # 8 pairs per thread, two phases
+    (dict(op="LSTM", direction="forward", S=5, Bt=50, I=20, H=72, with_lens=True, with_p=True,
+          clip=0.8), 24),                               # 6 pairs per thread, one phase
+]
+
+
+@pytest.mark.parametrize("k", range(len(EIGHT_PAIRS)))
+def test_eight_pair_streamed_kernel_matches_oracle(k):
+    spec, units = dict(EIGHT_PAIRS[k][0]), EIGHT_PAIRS[k][1]
+    op, direction = spec.pop("op"), spec.pop("direction")
+    S, Bt, I, H = spec.pop("S"), spec.pop("Bt"), spec.pop("I"), spec.pop("H")
+    kw = {key: spec.pop(key) for key in ("with_lens", "with_p") if key in spec}
+    c = workloads.random_case(op, direction, S, Bt, I, H, seed=900 + k, with_h0=True,
+                              with_c0=(op == "LSTM"), scale=min(0.6, 1.5 / H ** 0.5), **kw, **spec)
+    plan = ra.plan_for_case(c, units_per_block=units)
+    d = dict(kv.split("=", 1) for kv in plan.describe().split() if "=" in kv)
+    pairs = -(-int(d["BT"]) * int(d["U"]) // (64 * int(d["waves"])))
+    assert d["resident"] == "0" and pairs > 2, plan.describe()
+    say(f"case {c.name} units_per_block={units}: {plan.describe()}")
+    compare(c, run_gpu(c, plan=plan))
+
+
 def test_zero_length_rows_and_masks_bit_exact():
     c = workloads.random_case("LSTM", "bidirectional", 9, 19, 10, 24, seed=7, with_h0=True,
                               with_c0=True, lens=[0, 9, 1, 0, 5, 2, 9, 0, 3, 4, 8, 7, 6, 1, 0, 9, 2,
