@@ -8,7 +8,6 @@ file, where the Python binding loads it.
 """
 import concurrent.futures as cf
 import os
-import shutil
 import subprocess
 import sys
 
