@@ -26,19 +26,30 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-ffp-contract=off",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]
 
-# every .hip file of csrc (the step-loop instantiations are split over several
-# translation units so that they compile in parallel) and the HIP host code
-HIP_SOURCES = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip")) + ["run.cpp"]
-CXX_SOURCES = ["plan.cpp"]
+# The instantiation tables of the step loop: one source compiled once per
+# kernel family and activation set (recurrence_inst.hip), so that they
+# compile in parallel.
+INST = "recurrence_inst.hip"
+INST_UNITS = [(fam, act) for fam in range(4) for act in range(5)]
+
+# (source, extra flags, object name) of every translation unit: the .hip
+# files of csrc, the instantiation units, the HIP host code
+HIP_UNITS = ([(f, [], f + ".o") for f in sorted(os.listdir(CSRC))
+              if f.endswith(".hip") and f != INST] +
+             [(INST, [f"-DRNN_FAMILY={fam}", f"-DRNN_ACT={act}"],
+               f"recurrence_inst_f{fam}_a{act}.o") for fam, act in INST_UNITS] +
+             [("run.cpp", [], "run.cpp.o")])
+CXX_UNITS = [("plan.cpp", [], "plan.cpp.o")]
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, src + ".o")
+def _compile(unit, verbose):
+    src, extra, oname = unit
+    obj = os.path.join(BUILD, oname)
     path = os.path.join(CSRC, src)
-    if src in CXX_SOURCES:
-        cmd = ["g++", *COMMON, "-c", path, "-o", obj]
+    if unit in CXX_UNITS:
+        cmd = ["g++", *COMMON, *extra, "-c", path, "-o", obj]
     else:
-        cmd = [HIPCC, *COMMON, *HIP_FLAGS, "-x", "hip", "-c", path, "-o", obj]
+        cmd = [HIPCC, *COMMON, *HIP_FLAGS, *extra, "-x", "hip", "-c", path, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,7 +61,7 @@ def _compile(src, verbose):
 def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), HIP_SOURCES + CXX_SOURCES))
+        objs = list(ex.map(lambda u: _compile(u, verbose), HIP_UNITS + CXX_UNITS))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

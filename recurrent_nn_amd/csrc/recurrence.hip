@@ -1,6 +1,8 @@
 // recurrence.hip -- selection and launch of the step-loop kernels
-// (recurrence_kernel.h): the compiled shapes, the occupancy check of the
-// persistent (cooperative) form, and the launches.
+// (recurrence_kernel.h, recurrence_pipe.h, recurrence_exact.h): the compiled
+// shapes (tables in recurrence_inst.hip, one per kernel family and activation
+// set), the occupancy check of the persistent (cooperative) form, and the
+// launches.
 #include <hip/hip_runtime.h>
 
 #include "recurrence_exact.h"
