@@ -9,6 +9,7 @@ operator runs in the HIP library; if the library is missing, nothing runs.
 from __future__ import annotations
 
 import ctypes
+import sys
 from typing import Optional, Sequence, Tuple
 
 from . import _lib
@@ -172,12 +173,35 @@ class RNNPlan:
         _check(st, "rnn_plan_workspace_size")
         self._ws = None
 
-    def __del__(self):
+    def close(self) -> None:
+        """Release the plan (rnn_plan_destroy) and drop the workspace tensor.
+        Idempotent.  Call it, or use the plan as a context manager, before the
+        process exits: the library's HIP objects (timing events, the pinned
+        staging of sequence_lens) are then released while the HIP runtime is
+        still fully alive."""
+        plan, self.plan = getattr(self, "plan", None), None
+        self._ws = None
+        if plan:
+            rnn_plan_destroy(plan)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+        return False
+
+    def __del__(self, _finalizing=sys.is_finalizing):
+        # During interpreter shutdown the HIP runtime and the profiler hooks
+        # that wrap it may already be torn down (and this module's globals
+        # cleared): make no library call then; the process is ending and its
+        # memory goes with it.
+        if getattr(self, "plan", None) is None or _finalizing():
+            return
         try:
-            rnn_plan_destroy(getattr(self, "plan", None))
+            self.close()
         except Exception:
             pass
-        self.plan = None
 
     def describe(self) -> str:
         return rnn_plan_describe(self.plan)
@@ -299,8 +323,15 @@ def plan_for_case(case, **extra) -> RNNPlan:
 
 def run_case(case, plan: Optional[RNNPlan] = None, device="cuda", **extra):
     """Copy a CPU case to the device, run it, return (Y, Y_h, Y_c) device tensors."""
-    p = plan if plan is not None else plan_for_case(case, **extra)
+    own = plan is None
+    p = plan_for_case(case, **extra) if own else plan
     t = {k: (v.to(device) if v is not None and k != "sequence_lens" else v)
          for k, v in case.tensors().items()}
-    return p.run(t["X"], t["W"], t["R"], t["B"], t["sequence_lens"], t["initial_h"],
-                 t["initial_c"], t["P"])
+    try:
+        return p.run(t["X"], t["W"], t["R"], t["B"], t["sequence_lens"], t["initial_h"],
+                     t["initial_c"], t["P"])
+    finally:
+        if own:
+            # (torch's allocator keeps the workspace for work already enqueued
+            # on this stream; the plan's own staging is waited for on release)
+            p.close()
