@@ -3,14 +3,17 @@
 One step = one full operator invocation (weight pack, state init, the
 projection XW = X . W^T over all steps, the step loop with its gate
 arithmetic, masking and output writes) on one batch of synthetic input that
-is already resident in device memory.  The workload is the bidirectional LSTM
-(seq 512, batch 64, input 1024, hidden 1024, fp32, full-length sequences, no
-peepholes); its inputs are drawn by workloads.py.
+is already resident in device memory.  The headline workload is the
+bidirectional LSTM (seq 512, batch 64, input 1024, hidden 1024, fp32,
+full-length sequences, no peepholes); its inputs are drawn by workloads.py.
 
 Prints ONE JSON line: throughput in cell-updates/s (seq * batch * dirs per
-second), the roofline of the dominant kernel from HIP events recorded on the
-library's stream during extra timed runs, and the CPU oracle timed on a
-bounded sample of the same workload on the host's cores.
+second) of the headline workload; the roofline of its dominant kernel from
+HIP events recorded on the library's stream during extra timed runs, counted
+on the valid work (positions past a row's sequence length are not work of the
+method); the same figures for the other workloads of the list under
+"configs"; and the CPU oracle timed on a bounded sample of the headline
+workload on the host's cores.
 """
 from __future__ import annotations
 
@@ -43,6 +46,8 @@ def parse():
     p.add_argument("--kernel-path", type=int, default=0, help="0 auto, 1 persistent, 2 per step")
     p.add_argument("--cpu-budget-s", type=float, default=30.0, help="0 skips the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-configs", action="store_true",
+                   help="time only --workload, not the other workloads of the list")
     p.add_argument("--exact", action="store_true",
                    help="exact mode: k-ordered unfused products on the VALU (results bit-identical "
                         "to the oracle); reported against the fp32 vector peak")
@@ -160,8 +165,16 @@ def counter_summary(d):
     for name, did, ctr, v in _pmc_rows(d, counter=True):
         k = acc.setdefault(name, {}).setdefault(ctr, {})
         k[did] = k.get(did, 0.0) + v
-    out = {n: {c: {"mean": float(np.mean(list(v.values()))), "dispatches": len(v)}
-               for c, v in cs.items()} for n, cs in acc.items()}
+    # "steady": the dispatches after each kernel's first one (the first runs
+    # cold: instruction cache, TLB, clocks ramping up)
+    def stats(v):
+        ids = sorted(v)
+        vals = [v[i] for i in ids]
+        st = vals[1:] if len(vals) > 1 else vals
+        return {"mean": float(np.mean(vals)), "first": vals[0],
+                "steady_mean": float(np.mean(st)), "steady_min": float(np.min(st)),
+                "steady_max": float(np.max(st)), "dispatches": len(vals)}
+    out = {n: {c: stats(v) for c, v in cs.items()} for n, cs in acc.items()}
     print(json.dumps(out, indent=1))
 
 
@@ -216,13 +229,37 @@ def measured_traffic(workload, stage):
 
 
 def flops_per_run(c):
-    """Algorithmic FLOPs of the two products of one invocation (every step of
-    every row, i.e. the nominal work; GRU lbr=0's two products per step have
-    the same total as one G*H-wide product)."""
+    """Algorithmic FLOPs of the two products of one invocation, as
+    (projection, recurrence) for the nominal work (every step of every row)
+    and for the valid work (D * sum(len_b) steps: positions past a row's
+    length are never computed by the method; without sequence_lens the two
+    are equal).  GRU lbr=0's two products per step have the same total as one
+    G*H-wide product."""
     D, G = c.dirs, c.gates
-    proj = 2.0 * c.seq * c.batch * D * G * c.hidden * c.input
-    rec = 2.0 * c.seq * c.batch * D * G * c.hidden * c.hidden
-    return proj, rec
+    nominal_steps = c.seq * c.batch * D
+    valid_steps = c.valid_cell_updates()
+    per_proj = 2.0 * G * c.hidden * c.input
+    per_rec = 2.0 * G * c.hidden * c.hidden
+    return {"nominal": (per_proj * nominal_steps, per_rec * nominal_steps),
+            "valid": (per_proj * valid_steps, per_rec * valid_steps)}
+
+
+def host_facts():
+    """The host's CPU model and counts (the CPU baseline's context)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = None
+    return {"cpu_model": model, "host_logical_cpus": os.cpu_count(), "affinity_cpus": aff}
 
 
 def cpu_baseline(c, budget_s):
@@ -248,10 +285,125 @@ def cpu_baseline(c, budget_s):
             dt = time.perf_counter() - t0
             if dt >= 10.0 or dt + dt / reps > budget_s:
                 break
+    hf = host_facts()
     return {"value": cells * reps / dt, "unit": "cell-updates/s", "cores": nt, "kind": "oracle",
             "sample": f"the whole workload ({c.batch} rows x {c.seq} steps x {c.dirs} directions "
                       f"= {cells} cell-updates) run {reps} time(s) in {dt:.1f} s on {nt} threads",
-            "seconds": dt}
+            "threads": nt, **hf, "seconds": dt}
+
+
+def measure(c, steps, warmup, dev, kernel_path=0, exact=False, time_chunk=0, stage_runs=None):
+    """Run one workload on the GPU: warm-up, exactly `steps` invocations
+    between two events on the stream (the timed region), per-stage durations
+    from the library's own events over further runs, and each invocation
+    between its own events (median, minimum).  Inputs are resident in device
+    memory before the timed region starts.  The plan is released before
+    returning."""
+    import numpy as np
+    import torch
+
+    import recurrent_nn_amd as ra
+
+    t = {k: (v.to(dev) if v is not None and k != "sequence_lens" else v)
+         for k, v in c.tensors().items()}
+    stream = torch.cuda.current_stream(dev)
+    with ra.plan_for_case(c, kernel_path=kernel_path, exact=exact,
+                          time_chunk=time_chunk) as plan:
+        Y = torch.empty(plan.output_shapes()[0], dtype=torch.float32, device=dev)
+        Yh = torch.empty(plan.output_shapes()[1], dtype=torch.float32, device=dev)
+        Yc = torch.empty_like(Yh) if c.op == "LSTM" else None
+        out = (Y, Yh, Yc)
+
+        def step():
+            plan.run(t["X"], t["W"], t["R"], t["B"], t["sequence_lens"], t["initial_h"],
+                     t["initial_c"], t["P"], out=out, stream=stream)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        plan.check(stream)
+        desc = plan.describe()
+        print(f"[bench] {c.name}: {desc}", file=sys.stderr, flush=True)
+
+        # ---- the timed region: exactly `steps` invocations ------------------
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = e0.elapsed_time(e1) / steps
+        print(f"[bench] {c.name}: {steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s)",
+              file=sys.stderr, flush=True)
+
+        # ---- per-stage durations from HIP events on the library's stream -----
+        plan.enable_timing(True)
+        per = {k: [] for k in ra.STAGES}
+        for _ in range(stage_runs if stage_runs else max(3, steps)):
+            step()
+            for k, v in plan.last_timings().items():
+                per[k].append(v)
+        plan.enable_timing(False)
+        torch.cuda.synchronize()
+        plan.check(stream)
+        stage_ms = {k: float(np.mean(v)) for k, v in per.items()}
+
+        # ---- each invocation between its own events --------------------------
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a_, b_ in evs:
+            a_.record(stream)
+            step()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        each = sorted(a_.elapsed_time(b_) for a_, b_ in evs)
+    del t, out, Y, Yh, Yc
+    return {"ms": ms, "wall_s": wall, "stage_ms": stage_ms, "median": each[len(each) // 2],
+            "min": each[0], "plan": desc}
+
+
+def kernel_figures(c, m, exact=False):
+    """Roofline figures of the projection and the step loop of one measured
+    workload: achieved TFLOP/s and the fraction of the peak for the valid work
+    (what the method computes) and for the nominal work (every step of every
+    row)."""
+    fl = flops_per_run(c)
+    proj_peak = BF16_MFMA_PEAK_TFLOPS if c.proj_bf16 else FP32_MFMA_PEAK_TFLOPS
+    rec_peak = FP32_MFMA_PEAK_TFLOPS
+    bound = "mfma"
+    if exact:
+        proj_peak = rec_peak = FP32_VALU_MULADD_PEAK_TFLOPS
+        bound = "alu"
+    out = {}
+    for i, (k, peak) in enumerate((("projection", proj_peak), ("recurrence", rec_peak))):
+        ms = m["stage_ms"][k]
+        fv, fn = fl["valid"][i], fl["nominal"][i]
+        out[k] = {"bound": bound, "ms": ms, "peak": peak, "unit": "TFLOP/s",
+                  "flop_valid": fv, "flop_nominal": fn,
+                  "achieved": fv / (ms * 1e-3) / 1e12,
+                  "frac": fv / (ms * 1e-3) / 1e12 / peak,
+                  "achieved_nominal": fn / (ms * 1e-3) / 1e12,
+                  "frac_nominal": fn / (ms * 1e-3) / 1e12 / peak}
+    out["recurrence"]["us_per_step"] = m["stage_ms"]["recurrence"] * 1e3 / c.seq
+    return out
+
+
+def rounded(d):
+    if isinstance(d, dict):
+        return {k: rounded(v) for k, v in d.items()}
+    if isinstance(d, float):
+        return float(f"{d:.6g}")
+    return d
+
+
+# The five workloads of the operator's benchmark list; the first is timed as
+# the headline line, the others are reported under "configs".
+CONFIGS = ["lstm_bidir_s512_b64_i1024_h1024", "rnn_fwd_s4_b2_i3_h5", "lstm_bidir_s16_b4_i32_h64",
+           "gru_fwd_s128_b32_i256_h512_lbr0", "gru_fwd_s128_b32_i256_h512_lbr1",
+           "gru_rev_s256_b256_i2048_h2048_bf16"]
 
 
 def main():
@@ -263,9 +415,9 @@ def main():
         counter_summary(args.counter_summary)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "the step loop runs on one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1 "
+                                   "(the multi-GPU layout is a design, not an implementation)"}))
         sys.exit(2)
-    import numpy as np
     import torch
 
     import recurrent_nn_amd as ra
@@ -285,98 +437,30 @@ def main():
     torch.cuda.set_device(dev)
     c = workloads.workload(args.workload)
     print(f"[bench] workload {c.name}: inputs drawn", file=sys.stderr, flush=True)
-    t = {k: (v.to(dev) if v is not None and k != "sequence_lens" else v)
-         for k, v in c.tensors().items()}
-    plan = ra.plan_for_case(c, kernel_path=args.kernel_path, exact=args.exact,
-                            time_chunk=args.time_chunk)
-    Y = torch.empty(plan.output_shapes()[0], dtype=torch.float32, device=dev)
-    Yh = torch.empty(plan.output_shapes()[1], dtype=torch.float32, device=dev)
-    Yc = torch.empty_like(Yh) if c.op == "LSTM" else None
-    out = (Y, Yh, Yc)
-    stream = torch.cuda.current_stream(dev)
-
-    def step():
-        plan.run(t["X"], t["W"], t["R"], t["B"], t["sequence_lens"], t["initial_h"],
-                 t["initial_c"], t["P"], out=out, stream=stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    plan.check(stream)
-    print(f"[bench] {plan.describe()}", file=sys.stderr, flush=True)
-
-    # ---- the timed region: exactly K steps ---------------------------------
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] {args.steps} steps: {ms:.3f} ms/step (wall {wall:.3f} s)",
-          file=sys.stderr, flush=True)
-
-    # ---- per-kernel durations from HIP events on the library's stream -------
-    plan.enable_timing(True)
-    per = {k: [] for k in ra.STAGES}
-    for _ in range(max(3, args.steps)):
-        step()
-        for k, v in plan.last_timings().items():
-            per[k].append(v)
-    plan.enable_timing(False)
-    torch.cuda.synchronize()
-    plan.check(stream)
-    stage_ms = {k: float(np.mean(v)) for k, v in per.items()}
-    print(f"[bench] stage ms: {json.dumps(stage_ms)}", file=sys.stderr, flush=True)
-
-    # ---- each invocation timed on its own, for the median and the minimum ----
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a_, b_ in evs:
-        a_.record(stream)
-        step()
-        b_.record(stream)
-    torch.cuda.synchronize()
-    each = sorted(a_.elapsed_time(b_) for a_, b_ in evs)
-
-    proj_f, rec_f = flops_per_run(c)
-    proj_peak = BF16_MFMA_PEAK_TFLOPS if c.proj_bf16 else FP32_MFMA_PEAK_TFLOPS
-    bound = "mfma"
-    if args.exact:
-        proj_peak = rec_peak = FP32_VALU_MULADD_PEAK_TFLOPS
-        bound = "alu"
-    else:
-        rec_peak = FP32_MFMA_PEAK_TFLOPS
-    kernels = {
-        "projection": {"bound": bound, "flop": proj_f, "ms": stage_ms["projection"],
-                       "achieved": proj_f / (stage_ms["projection"] * 1e-3) / 1e12,
-                       "peak": proj_peak, "unit": "TFLOP/s"},
-        "recurrence": {"bound": bound, "flop": rec_f, "ms": stage_ms["recurrence"],
-                       "achieved": rec_f / (stage_ms["recurrence"] * 1e-3) / 1e12,
-                       "peak": rec_peak, "unit": "TFLOP/s",
-                       "us_per_step": stage_ms["recurrence"] * 1e3 / c.seq},
-    }
-    for k in kernels.values():
-        k["frac"] = k["achieved"] / k["peak"]
-    # the recurrence's operand streams per step: R (what a kernel that streamed
-    # it would need, against HBM) and the H rows every workgroup reads (L2)
-    desc = dict(kv.split("=", 1) for kv in plan.describe().split() if "=" in kv)
-    t_step = stage_ms["recurrence"] * 1e-3 / c.seq
+    m = measure(c, args.steps, args.warmup, dev, kernel_path=args.kernel_path, exact=args.exact,
+                time_chunk=args.time_chunk)
+    print(f"[bench] stage ms: {json.dumps(m['stage_ms'])}", file=sys.stderr, flush=True)
+    kernels = kernel_figures(c, m, exact=args.exact)
+    # size-derived rates of the step loop's operand streams (sizes over the
+    # step time; not counter readings): R bytes per step (what a kernel that
+    # streamed R would need from HBM) and the H rows every workgroup reads
+    desc = dict(kv.split("=", 1) for kv in m["plan"].split() if "=" in kv)
+    t_step = m["stage_ms"]["recurrence"] * 1e-3 / c.seq
     r_bytes = 4.0 * c.dirs * c.gates * c.hidden * c.hidden
     h_bytes = 4.0 * int(desc["workgroups"]) * int(desc["BT"]) * int(desc["Hp"])
-    kernels["recurrence"]["r_stream_gbs"] = r_bytes / t_step / 1e9
-    kernels["recurrence"]["r_stream_frac_hbm"] = r_bytes / t_step / (HBM_PEAK_GBS * 1e9)
-    kernels["recurrence"]["h_broadcast_gbs"] = h_bytes / t_step / 1e9
-    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    kernels["recurrence"]["size_derived"] = {
+        "note": "operand bytes per step divided by the step time; not counter readings",
+        "r_bytes_per_step": r_bytes, "r_gbs": r_bytes / t_step / 1e9,
+        "r_frac_of_hbm": r_bytes / t_step / (HBM_PEAK_GBS * 1e9),
+        "h_rows_read_bytes_per_step": h_bytes, "h_rows_read_gbs": h_bytes / t_step / 1e9}
+    dom = max(("projection", "recurrence"), key=lambda k: kernels[k]["ms"])
     dk = kernels[dom]
     roofline = {"bound": dk["bound"], "achieved": round(dk["achieved"], 3), "peak": dk["peak"],
                 "unit": dk["unit"], "frac": round(dk["frac"], 4),
-                "traffic": measured_traffic(c.name, dom),
-                "kernel": dom}
+                "traffic": measured_traffic(c.name, dom), "kernel": dom,
+                "work": "valid (sum of sequence lengths x directions steps)"}
 
+    ms = m["ms"]
     cells = c.cell_updates()
     value = cells / (ms * 1e-3)
     res = {
@@ -388,20 +472,41 @@ def main():
                    "time_chunk": args.time_chunk, "op": c.op, "direction": c.direction, "seq": c.seq,
                    "batch": c.batch, "input": c.input, "hidden": c.hidden, "dirs": c.dirs,
                    "layout": c.layout, "global_batch": c.batch, "seq_len": c.seq,
-                   "parallelism": "none (1 GPU)", "plan": plan.describe()},
+                   "parallelism": "none (1 GPU)", "plan": m["plan"]},
         "valid_cell_updates_per_s": c.valid_cell_updates() / (ms * 1e-3),
-        "ms_per_step_median": each[len(each) // 2], "ms_per_step_min": each[0],
+        "ms_per_step_median": m["median"], "ms_per_step_min": m["min"],
         "inputs_sha256": c.digests(),
         "roofline": roofline,
-        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
-                        for kk, vv in v.items()} for k, v in kernels.items()},
-        "stage_ms": stage_ms,
+        "kernels": rounded(kernels),
+        "stage_ms": m["stage_ms"],
     }
+    del c
+    # ---- the other workloads of the list, same protocol, fewer runs ---------
+    if not args.no_configs and not args.exact and not args.time_chunk:
+        confs = {}
+        for name in CONFIGS:
+            if name == args.workload:
+                continue
+            cc = workloads.workload(name)
+            steps_c = max(5, min(args.steps, 20))
+            mc = measure(cc, steps_c, 3, dev)
+            kc = kernel_figures(cc, mc)
+            confs[name] = rounded({
+                "ms_per_step": mc["ms"], "ms_median": mc["median"], "ms_min": mc["min"],
+                "cell_updates_per_s": cc.cell_updates() / (mc["ms"] * 1e-3),
+                "valid_cell_updates_per_s": cc.valid_cell_updates() / (mc["ms"] * 1e-3),
+                "steps": steps_c, "stage_ms": mc["stage_ms"], "kernels": kc, "plan": mc["plan"],
+                "inputs_sha256": cc.digests()})
+            del cc
+        res["configs"] = confs
     if not args.no_cpu_baseline and args.cpu_budget_s > 0:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cb = cpu_baseline(c, args.cpu_budget_s)
-        res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        cb = cpu_baseline(workloads.workload(args.workload), args.cpu_budget_s)
+        res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample",
+                                                  "threads", "cpu_model", "host_logical_cpus",
+                                                  "affinity_cpus")}
         res["gpu_over_cpu_baseline"] = value / cb["value"]
+    torch.cuda.synchronize()
     print(json.dumps(res), flush=True)
 
 

@@ -115,7 +115,13 @@ def _floats(vals):
 
 
 def default_threads() -> int:
-    return max(1, min(os.cpu_count() or 1, 16))
+    """Threads the oracle uses by default: the CPUs this process may run on,
+    at most 16 (a one-GPU share of a GPU host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
 
 
 def run(case, n_threads: Optional[int] = None, want_y: bool = True,
