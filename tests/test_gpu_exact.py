@@ -13,7 +13,7 @@ import torch
 import oracle
 import recurrent_nn_amd as ra
 import workloads
-from tests.test_gpu_parity import FEATURES, check_masks, run_gpu, say
+from tests.test_gpu_parity import FEATURES, check_masks, oracle_outputs, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -80,21 +80,15 @@ def test_exact_results_do_not_depend_on_tiling_launch_or_chunks():
         assert_bit_exact(c, run_gpu(c, exact=True, **extra), ref)
 
 
-def test_lstm_bench_shape_sampled_rows_bit_exact():
-    rows = [0, 29, 63]
-    full = workloads.workload("lstm_bidir_s512_b64_i1024_h1024")
-    say(f"case {full.name} exact, rows {rows}")
-    Y, Yh, Yc = run_gpu(full, exact=True)
-    sub = workloads.select_rows(full, rows)
-    ref = oracle.run(sub)[1:]
-    assert_bit_exact(sub, (Y[:, :, rows], Yh[:, rows], Yc[:, rows]), ref)
+def test_lstm_bench_workload_bit_exact_every_element():
+    name = "lstm_bidir_s512_b64_i1024_h1024"
+    c = workloads.workload(name)
+    say(f"case {name} exact, every element")
+    assert_bit_exact(c, run_gpu(c, exact=True), oracle_outputs(c, name))
 
 
-def test_gru_bf16_projection_sampled_rows_bit_exact():
-    rows = [0, 100, 255]
-    full = workloads.workload("gru_rev_s256_b256_i2048_h2048_bf16")
-    say(f"case {full.name} exact, rows {rows}")
-    Y, Yh, _ = run_gpu(full, exact=True)
-    sub = workloads.select_rows(full, rows)
-    ref = oracle.run(sub)[1:]
-    assert_bit_exact(sub, (Y[:, :, rows], Yh[:, rows], None), ref)
+def test_gru_bf16_workload_bit_exact_every_element():
+    name = "gru_rev_s256_b256_i2048_h2048_bf16"
+    c = workloads.workload(name)
+    say(f"case {name} exact, every element")
+    assert_bit_exact(c, run_gpu(c, exact=True), oracle_outputs(c, name))
