@@ -10,7 +10,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "librecurrent_nn_amd.so")
+# RNN_AMD_LIB names another build of the same library (the host-sanitizer
+# build of the CPU test suite); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("RNN_AMD_LIB") or os.path.join(HERE, "librecurrent_nn_amd.so")
 
 RNN_OK, RNN_ERR_INVALID_INPUT, RNN_ERR_UNSUPPORTED, RNN_ERR_DEVICE, RNN_ERR_OUT_OF_MEMORY = range(5)
 RNN_OP_RNN, RNN_OP_GRU, RNN_OP_LSTM = 0, 1, 2
