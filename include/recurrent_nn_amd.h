@@ -141,13 +141,27 @@ typedef struct rnn_plan rnn_plan;
  * activations (f, g, h per direction with alpha/beta cursors), choose the
  * tiling and lay out the workspace.  Host only: touches no device.
  *   attrs, dims: read during the call only.  *out receives a new plan.
- *   Errors: RNN_ERR_INVALID_INPUT (unknown op/direction/activation name, wrong
- *   activation count, num_directions not matching direction, layout not 0/1,
- *   hidden 0 or not equal to hidden_size, input_forget on a non-LSTM,
- *   linear_before_reset on a non-GRU, negative sizes or time_chunk);
+ *   Errors, each with the passage that defines the rule (sections of the
+ *   onemodel page "Recurrent operators: RNN, GRU, LSTM" unless stated):
+ *   RNN_ERR_INVALID_INPUT for
+ *     - an activation name outside the supported list, or a list that is
+ *       neither one set nor (bidirectional) a forward and a reverse set
+ *       .................................................. "Activations";
+ *     - hidden 0, or a hidden_size attribute that differs from R's last
+ *       dimension ....... "Choices the specification leaves open", hidden_size;
+ *     - input_forget on a non-LSTM, linear_before_reset on a non-GRU (the
+ *       attributes exist for those operators only) ......... "Computation";
+ *     - layout other than 0 or 1 ..... "Choices ...", layout = 1; WebGPU README
+ *       "Attributes";
+ *     - an unknown op or direction, num_directions not matching direction
+ *       (W's first dimension is the direction count) ..... WebGPU README
+ *       "Inputs" and "Attributes";
+ *     - negative sizes, time_chunk, barrier_spin_limit or tiling overrides
+ *       outside their ranges (this library's own attributes);
  *   RNN_ERR_UNSUPPORTED when, per direction, L*batch*G*hidden + 4*batch*hidden
  *   (+ G*hidden*(input+hidden) unless constant_weights) reaches 2^30 floats,
- *   with L = seq_length, or the chunk length when time_chunk is set.
+ *   with L = seq_length, or the chunk length when time_chunk is set
+ *   ............................................................... "Limits".
  */
 rnn_status rnn_plan_create(const rnn_attrs *attrs, const rnn_dims *dims, rnn_plan **out);
 
@@ -168,10 +182,15 @@ rnn_status rnn_plan_workspace_size(const rnn_plan *plan, size_t *bytes);
  *   256-byte aligned, owned by the caller, used by this run until the stream
  *   passes it.  With constant_weights the packed weights stay in it between
  *   runs: reuse the same workspace and weight pointers.
- *   Errors (nothing is enqueued): RNN_ERR_INVALID_INPUT for NULL required
- *   pointers, misaligned pointers, a small workspace, a length outside
- *   [0, seq], Y_c/initial_c/P given to a non-LSTM plan; RNN_ERR_DEVICE when a
- *   HIP call fails (the run may then be partial).
+ *   Errors (nothing is enqueued): RNN_ERR_INVALID_INPUT for
+ *     - a sequence length outside [0, seq] ..... "Choices the specification
+ *       leaves open", sequence_lens (the run-time InvalidInput it names);
+ *     - Y_c, initial_c or P given to a non-LSTM plan (LSTM-only tensors)
+ *       ...................................... "Support"; WebGPU README "Inputs";
+ *     - NULL X, W or R (required inputs) ........... WebGPU README "Inputs";
+ *     - misaligned pointers or a workspace missing, too small or misaligned
+ *       (this library's own conventions, above);
+ *   RNN_ERR_DEVICE when a HIP call fails (the run may then be partial).
  */
 rnn_status rnn_run(rnn_plan *plan, void *hip_stream, void *workspace, size_t workspace_bytes,
                    const float *X, const float *W, const float *R, const float *B,

@@ -123,7 +123,9 @@ __device__ __forceinline__ float clip_pre(float x, int on, float c)
     return y < nc ? nc : y;
 }
 
-// Every NaN in Y, Y_h and Y_c is written as 0x7FC00000.
+// The outputs carry one NaN encoding only (onemodel "Recurrent operators",
+// section "Exact mode"): any NaN becomes the quiet NaN with bit pattern
+// 0x7FC00000 (positive sign, no payload) when Y, Y_h or Y_c is stored.
 __device__ __forceinline__ float canon_nan(float v)
 {
     return v != v ? __uint_as_float(0x7FC00000u) : v;
