@@ -228,6 +228,32 @@ rnn_status rnn_cell_run(rnn_plan *plan, void *hip_stream, void *workspace, size_
                         float *C_out);
 
 /*
+ * rnn_run_noalloc -- rnn_run for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without a workspace, the same launches and
+ * results, and no allocating call at all.  Its scratch is a device array of
+ * RNN_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; sequence_lens reach the device as kernel arguments.
+ *   Limits (RNN_ERR_UNSUPPORTED, nothing enqueued, no device call made): a plan
+ *   whose rnn_plan_workspace_size() exceeds RNN_NOALLOC_SCRATCH_BYTES, or
+ *   sequence_lens with more than RNN_NOALLOC_MAX_LENS_BATCH batch rows.
+ *   Sharing: every call on one GPU uses that GPU's one scratch array, and each
+ *   call leaves it holding its own state; calls that overlap in time on the
+ *   same GPU (another stream, another thread, another plan) race and give
+ *   undefined results.  Serialise them.  With constant_weights the packed
+ *   weights are reused only while no other plan has run here in between.
+ *   Stage timing (rnn_plan_enable_timing) records nothing on this path, and a
+ *   barrier time-out is not reported (rnn_workspace_check needs a workspace).
+ *   Other errors: those of rnn_run.
+ */
+#define RNN_NOALLOC_SCRATCH_BYTES (64u << 20)
+#define RNN_NOALLOC_MAX_LENS_BATCH 256
+rnn_status rnn_run_noalloc(rnn_plan *plan, void *hip_stream, const float *X, const float *W,
+                           const float *R, const float *B, const int32_t *sequence_lens,
+                           const float *initial_h, const float *initial_c, const float *P,
+                           float *Y, float *Y_h, float *Y_c);
+
+/*
  * rnn_workspace_check -- wait for `hip_stream`, then read the device-side
  * error word that the last run on this workspace left (a step barrier that
  * timed out).  RNN_OK when clean, RNN_ERR_DEVICE otherwise.  For tests of

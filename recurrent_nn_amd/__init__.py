@@ -16,7 +16,8 @@ from . import _lib
 from ._lib import (RNN_OK, RNN_ERR_INVALID_INPUT, RNN_ERR_UNSUPPORTED, RNN_ERR_DEVICE,  # noqa: F401
                    RNN_ERR_OUT_OF_MEMORY, RNN_OP_RNN, RNN_OP_GRU, RNN_OP_LSTM, RNN_PROJ_F32,
                    RNN_PROJ_BF16, RNN_PATH_AUTO, RNN_PATH_PERSISTENT, RNN_PATH_PER_STEP,
-                   STATUS_NAMES, rnn_attrs, rnn_dims)
+                   RNN_NOALLOC_SCRATCH_BYTES, RNN_NOALLOC_MAX_LENS_BATCH, STATUS_NAMES,
+                   rnn_attrs, rnn_dims)
 
 OPS = {"RNN": RNN_OP_RNN, "GRU": RNN_OP_GRU, "LSTM": RNN_OP_LSTM}
 STAGES = ("pack", "projection", "recurrence", "other")
@@ -59,14 +60,26 @@ def rnn_run(plan: int, stream: int, workspace: int, workspace_bytes: int, X: int
             Y: int = 0, Y_h: int = 0, Y_c: int = 0) -> int:
     """Device pointers as ints (0 = NULL); sequence_lens a host int32 array
     object exposing ctypes (numpy array, ctypes array) or None."""
+    return _lib.load().rnn_run(plan, stream, workspace, workspace_bytes, X, W, R, B,
+                               _lens_ptr(sequence_lens), initial_h, initial_c, P, Y, Y_h, Y_c)
+
+
+def _lens_ptr(sequence_lens):
     lens_p = ctypes.POINTER(ctypes.c_int32)()
     if sequence_lens is not None:
         if hasattr(sequence_lens, "ctypes"):
             lens_p = sequence_lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
         else:
             lens_p = ctypes.cast(sequence_lens, ctypes.POINTER(ctypes.c_int32))
-    return _lib.load().rnn_run(plan, stream, workspace, workspace_bytes, X, W, R, B, lens_p,
-                               initial_h, initial_c, P, Y, Y_h, Y_c)
+    return lens_p
+
+
+def rnn_run_noalloc(plan: int, stream: int, X: int, W: int, R: int, B: int = 0,
+                    sequence_lens=None, initial_h: int = 0, initial_c: int = 0, P: int = 0,
+                    Y: int = 0, Y_h: int = 0, Y_c: int = 0) -> int:
+    """rnn_run without a workspace (the library's own per-GPU scratch)."""
+    return _lib.load().rnn_run_noalloc(plan, stream, X, W, R, B, _lens_ptr(sequence_lens),
+                                       initial_h, initial_c, P, Y, Y_h, Y_c)
 
 
 def rnn_cell_run(plan: int, stream: int, workspace: int, workspace_bytes: int, X: int, H: int,
@@ -240,10 +253,11 @@ class RNNPlan:
 
     def run(self, X, W, R, B=None, sequence_lens=None, initial_h=None, initial_c=None, P=None,
             want_y: bool = True, want_yh: bool = True, want_yc: Optional[bool] = None,
-            out=None, stream=None):
+            out=None, stream=None, noalloc: bool = False):
         """Enqueue one invocation on `stream` (default: torch's current stream).
         sequence_lens: host int32 tensor/array or None.  `out` may supply
-        preallocated (Y, Y_h, Y_c)."""
+        preallocated (Y, Y_h, Y_c).  noalloc: through rnn_run_noalloc (no
+        workspace; with `out` given, nothing is allocated at all)."""
         import numpy as np
         import torch
         for name, t in (("X", X), ("W", W), ("R", R), ("B", B), ("initial_h", initial_h),
@@ -266,8 +280,15 @@ class RNNPlan:
             if hasattr(sequence_lens, "numpy"):
                 sequence_lens = sequence_lens.cpu().numpy()
             lens = np.ascontiguousarray(sequence_lens, dtype=np.int32)
-        ws = self.workspace(dev)
         s = stream if stream is not None else torch.cuda.current_stream(dev)
+        if noalloc:
+            st = rnn_run_noalloc(self.plan, s.cuda_stream, self._ptr(X), self._ptr(W),
+                                 self._ptr(R), self._ptr(B), lens, self._ptr(initial_h),
+                                 self._ptr(initial_c), self._ptr(P), self._ptr(Y), self._ptr(Yh),
+                                 self._ptr(Yc))
+            _check(st, "rnn_run_noalloc")
+            return Y, Yh, Yc
+        ws = self.workspace(dev)
         st = rnn_run(self.plan, s.cuda_stream, self._ptr(ws), self.workspace_bytes,
                      self._ptr(X), self._ptr(W), self._ptr(R), self._ptr(B), lens,
                      self._ptr(initial_h), self._ptr(initial_c), self._ptr(P),

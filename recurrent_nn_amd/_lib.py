@@ -18,12 +18,14 @@ RNN_OK, RNN_ERR_INVALID_INPUT, RNN_ERR_UNSUPPORTED, RNN_ERR_DEVICE, RNN_ERR_OUT_
 RNN_OP_RNN, RNN_OP_GRU, RNN_OP_LSTM = 0, 1, 2
 RNN_PROJ_F32, RNN_PROJ_BF16 = 0, 1
 RNN_PATH_AUTO, RNN_PATH_PERSISTENT, RNN_PATH_PER_STEP = 0, 1, 2
+RNN_NOALLOC_SCRATCH_BYTES = 64 << 20     # include/recurrent_nn_amd.h
+RNN_NOALLOC_MAX_LENS_BATCH = 256
 
 STATUS_NAMES = {0: "RNN_OK", 1: "RNN_ERR_INVALID_INPUT", 2: "RNN_ERR_UNSUPPORTED",
                 3: "RNN_ERR_DEVICE", 4: "RNN_ERR_OUT_OF_MEMORY"}
 
 EXPORTED = ["rnn_plan_create", "rnn_plan_workspace_size", "rnn_run", "rnn_cell_run",
-            "rnn_workspace_check",
+            "rnn_run_noalloc", "rnn_workspace_check",
             "rnn_plan_enable_timing", "rnn_plan_last_timings", "rnn_plan_describe",
             "rnn_plan_destroy", "rnn_last_error"]
 
@@ -91,6 +93,9 @@ def load() -> ctypes.CDLL:
                           vp, vp, vp, vp, vp, vp]
     L.rnn_cell_run.restype = i32
     L.rnn_cell_run.argtypes = [vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.rnn_run_noalloc.restype = i32
+    L.rnn_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_int32),
+                                  vp, vp, vp, vp, vp, vp]
     L.rnn_workspace_check.restype = i32
     L.rnn_workspace_check.argtypes = [vp, vp, vp]
     L.rnn_plan_enable_timing.restype = i32

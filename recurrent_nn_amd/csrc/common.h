@@ -150,6 +150,18 @@ struct InitArgs {
 };
 int launch_init(const InitArgs &a, void *stream);
 
+// Sequence lengths handed to the device as kernel arguments (no staging
+// buffer, no copy): the lengths by position and the batch row at each
+// position, for at most kInlineRows rows.
+constexpr int kInlineRows = 256;
+struct InlineLens {
+    int32_t n;
+    int32_t lens[kInlineRows];
+    int32_t order[kInlineRows];
+};
+// dst[0, n) = lens, dst[n, 2n) = order
+int launch_lens_inline(const InlineLens &l, int32_t *dst, void *stream);
+
 struct ProjArgs {
     const void *X;          // f32 X in the operator's layout
     uint16_t *Xb;           // bf16 projection: [D][steps * Bt][K] staging of the gathered rows

@@ -173,6 +173,22 @@ int launch_init(const InitArgs &a, void *stream)
     return (int)hipGetLastError();
 }
 
+__global__ void lens_inline_kernel(InlineLens l, int32_t *dst)
+{
+    for (int i = threadIdx.x; i < l.n; i += blockDim.x) {
+        dst[i] = l.lens[i];
+        dst[l.n + i] = l.order[i];
+    }
+}
+
+int launch_lens_inline(const InlineLens &l, int32_t *dst, void *stream)
+{
+    if (l.n < 1 || l.n > kInlineRows)
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(lens_inline_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, l, dst);
+    return (int)hipGetLastError();
+}
+
 __device__ __forceinline__ float canon0(float v)
 {
     return v != v ? __uint_as_float(0x7FC00000u) : v;

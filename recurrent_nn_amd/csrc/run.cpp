@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -30,14 +31,15 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 struct Timer {
     rnn_plan *p;
     hipStream_t s;
+    bool on;
     void begin(int stage)
     {
-        if (p->timing)
+        if (on)
             (void)hipEventRecord((hipEvent_t)p->events[2 * stage], s);
     }
     void end(int stage)
     {
-        if (p->timing)
+        if (on)
             (void)hipEventRecord((hipEvent_t)p->events[2 * stage + 1], s);
     }
 };
@@ -116,18 +118,34 @@ rnn_status device_setup(rnn_plan *p, unsigned char *ws)
         set_error("persistent path requested but the workgroups cannot all be resident");
         return RNN_ERR_UNSUPPORTED;
     }
-    if (p->timing) {
-        for (int i = 0; i < 2 * STAGE_COUNT; ++i)
-            if (!p->events[i]) {
-                hipEvent_t ev;
-                e = hipEventCreate(&ev);
-                if (e != hipSuccess)
-                    return hip_fail(e, "hipEventCreate");
-                p->events[i] = ev;
-            }
-    }
     p->dev_ready = 1;
     return RNN_OK;
+}
+
+// The timing events of the stages (created once, when timing is enabled).
+rnn_status ensure_events(rnn_plan *p)
+{
+    for (int i = 0; i < 2 * STAGE_COUNT; ++i)
+        if (!p->events[i]) {
+            hipEvent_t ev;
+            hipError_t e = hipEventCreate(&ev);
+            if (e != hipSuccess)
+                return hip_fail(e, "hipEventCreate");
+            p->events[i] = ev;
+        }
+    return RNN_OK;
+}
+
+// The batch rows in order of decreasing length (ties by row): order[i] is
+// the row held at position i and byPos[i] its length.  The kernels hold rows
+// in this order, so that the rows still active at a step come first.
+void order_rows(const int32_t *lens, int64_t Bt, int32_t *byPos, int32_t *order)
+{
+    for (int64_t b = 0; b < Bt; ++b)
+        order[b] = (int32_t)b;
+    std::stable_sort(order, order + Bt, [lens](int32_t x, int32_t y) { return lens[x] > lens[y]; });
+    for (int64_t i = 0; i < Bt; ++i)
+        byPos[i] = lens[order[i]];
 }
 
 
@@ -136,7 +154,7 @@ rnn_status run_checks(const rnn_plan *p, const void *workspace, size_t workspace
                       const float *X, const float *W, const float *R, const float *B,
                       const int32_t *sequence_lens, const float *initial_h,
                       const float *initial_c, const float *P, const float *Y, const float *Y_h,
-                      const float *Y_c)
+                      const float *Y_c, bool check_workspace = true)
 {
     const bool zero = p->S == 0 || p->Bt == 0;
     if (p->op != RNN_OP_LSTM && (initial_c || P || Y_c)) {
@@ -165,7 +183,8 @@ rnn_status run_checks(const rnn_plan *p, const void *workspace, size_t workspace
                 return RNN_ERR_INVALID_INPUT;
             }
 
-    if (!zero && (!workspace || workspace_bytes < p->ws.total || !aligned(workspace, 256))) {
+    if (check_workspace && !zero &&
+        (!workspace || workspace_bytes < p->ws.total || !aligned(workspace, 256))) {
         set_error("rnn_run: workspace missing, smaller than rnn_plan_workspace_size() or not "
                   "256-byte aligned");
         return RNN_ERR_INVALID_INPUT;
@@ -174,10 +193,14 @@ rnn_status run_checks(const rnn_plan *p, const void *workspace, size_t workspace
 }
 
 // The launch sequence of a checked run.
+// noalloc: the allocation-free form (rnn_run_noalloc): no stage timing, and
+// the sequence lengths reach the device as kernel arguments instead of
+// through the plan's pinned staging buffer.
 rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float *X,
                        const float *W, const float *R, const float *B,
                        const int32_t *sequence_lens, const float *initial_h,
-                       const float *initial_c, const float *P, float *Y, float *Y_h, float *Y_c)
+                       const float *initial_c, const float *P, float *Y, float *Y_h, float *Y_c,
+                       bool noalloc = false)
 {
     if (p->S == 0 || p->Bt == 0) {
         FinalArgs f{initial_h, initial_c, Y_h, Y_c, (int64_t)p->D * p->Bt * p->H};
@@ -190,8 +213,14 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
         return st;
     const bool persistent = p->kernel_path == RNN_PATH_PERSISTENT ||
                             (p->kernel_path == RNN_PATH_AUTO && p->can_persist);
-    Timer tm{p, s};
-    p->events_recorded = p->timing;
+    const bool timed = p->timing && !noalloc;
+    if (timed) {
+        st = ensure_events(p);
+        if (st != RNN_OK)
+            return st;
+    }
+    Timer tm{p, s, timed};
+    p->events_recorded = timed;
     hipError_t e;
 
     // 1. pack W (block-column row order, optional bf16) and R (padded tiles)
@@ -229,11 +258,18 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
     tm.begin(STAGE_OTHER);
     int32_t *lens_dev = (int32_t *)(ws + p->ws.lens);
     const int32_t *order_dev = nullptr;
-    if (sequence_lens) {
-        // the batch rows in order of decreasing length (ties by row) and
-        // their lengths in that order, staged in pinned memory owned by the
-        // plan: the kernels hold rows in this order, so that the rows still
-        // active at a step come first
+    if (sequence_lens && noalloc) {
+        // the lengths by position and the row order as kernel arguments
+        InlineLens il;
+        il.n = (int32_t)p->Bt;
+        order_rows(sequence_lens, p->Bt, il.lens, il.order);
+        int rc = launch_lens_inline(il, lens_dev, s);
+        if (rc)
+            return hip_fail((hipError_t)rc, "sequence_lens (kernel arguments)");
+        order_dev = lens_dev + p->Bt;
+    } else if (sequence_lens) {
+        // the lengths by position and the row order, staged in pinned memory
+        // owned by the plan and copied on the stream
         if (!p->lens_host) {
             e = hipHostMalloc((void **)&p->lens_host, (size_t)p->Bt * 3 * sizeof(int32_t),
                               hipHostMallocDefault);
@@ -251,13 +287,8 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
                 return hip_fail(e, "hipEventSynchronize (sequence_lens staging)");
             p->lens_pending = 0;
         }
-        int32_t *hl = p->lens_host, *hs = hl + p->Bt, *ho = hl + 2 * p->Bt;
-        std::memcpy(hl, sequence_lens, (size_t)p->Bt * sizeof(int32_t));
-        for (int64_t b = 0; b < p->Bt; ++b)
-            ho[b] = (int32_t)b;
-        std::stable_sort(ho, ho + p->Bt, [hl](int32_t x, int32_t y) { return hl[x] > hl[y]; });
-        for (int64_t i = 0; i < p->Bt; ++i)
-            hs[i] = hl[ho[i]];
+        int32_t *hs = p->lens_host, *ho = hs + p->Bt;   // by position, then the order
+        order_rows(sequence_lens, p->Bt, hs, ho);
         e = hipMemcpyAsync(lens_dev, hs, (size_t)p->Bt * 2 * sizeof(int32_t),
                            hipMemcpyHostToDevice, s);
         if (e != hipSuccess)
@@ -408,6 +439,93 @@ extern "C" rnn_status rnn_cell_run(rnn_plan *p, void *hip_stream, void *workspac
             return hip_fail((hipError_t)rc, "summed-bias expansion");
     }
     return run_enqueue(p, s, workspace, X, W, R, B, nullptr, H, C, P, nullptr, H_out, C_out);
+}
+
+// ---------------------------------------------------------------------------
+// rnn_run_noalloc: rnn_run without a caller workspace and without any
+// allocation.  Its scratch is one file-scope device array per GPU, of
+// RNN_NOALLOC_SCRATCH_BYTES; every call on a GPU shares that GPU's array (a
+// second call overlapping the first on the same GPU races with it).
+// ---------------------------------------------------------------------------
+namespace {
+
+static_assert(RNN_NOALLOC_MAX_LENS_BATCH == kInlineRows, "inline lengths limit");
+
+static __device__ __align__(256) unsigned char scratch[RNN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};   // device address of `scratch` on each GPU
+
+// The address of this GPU's copy of `scratch`, looked up once per device with
+// that device current.  In host code the array's own name is only a host-side
+// stand-in, so every use goes through the address kept here.
+rnn_status scratch_of_current_device(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) {
+        set_error("rnn_run_noalloc: device index beyond the library's table");
+        return RNN_ERR_UNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return hip_fail(e, "hipGetSymbolAddress (scratch)");
+        if (!ptr || !aligned(ptr, 256)) {
+            set_error("rnn_run_noalloc: scratch address is not 256-byte aligned");
+            return RNN_ERR_DEVICE;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return RNN_OK;
+}
+
+}  // namespace
+
+extern "C" rnn_status rnn_run_noalloc(rnn_plan *p, void *hip_stream, const float *X,
+                                      const float *W, const float *R, const float *B,
+                                      const int32_t *sequence_lens, const float *initial_h,
+                                      const float *initial_c, const float *P, float *Y,
+                                      float *Y_h, float *Y_c)
+{
+    set_error("");
+    if (!p) {
+        set_error("rnn_run_noalloc: NULL plan");
+        return RNN_ERR_INVALID_INPUT;
+    }
+    const bool zero = p->S == 0 || p->Bt == 0;
+    // the limits first: refused before any device call
+    if (!zero && p->ws.total > (size_t)RNN_NOALLOC_SCRATCH_BYTES) {
+        set_error("rnn_run_noalloc: this plan needs " + std::to_string(p->ws.total) +
+                  " bytes of scratch, more than the " +
+                  std::to_string((size_t)RNN_NOALLOC_SCRATCH_BYTES) +
+                  " the allocation-free entry point holds; use rnn_run with a workspace");
+        return RNN_ERR_UNSUPPORTED;
+    }
+    if (!zero && sequence_lens && p->Bt > RNN_NOALLOC_MAX_LENS_BATCH) {
+        set_error("rnn_run_noalloc: sequence_lens with more than " +
+                  std::to_string(RNN_NOALLOC_MAX_LENS_BATCH) +
+                  " batch rows; use rnn_run with a workspace");
+        return RNN_ERR_UNSUPPORTED;
+    }
+    void *ws = nullptr;
+    rnn_status st = run_checks(p, nullptr, 0, X, W, R, B, sequence_lens, initial_h, initial_c, P,
+                               Y, Y_h, Y_c, /*check_workspace=*/false);
+    if (st != RNN_OK)
+        return st;
+    if (!zero) {
+        st = scratch_of_current_device(&ws);
+        if (st != RNN_OK)
+            return st;
+    }
+    return run_enqueue(p, (hipStream_t)hip_stream, ws, X, W, R, B, sequence_lens, initial_h,
+                       initial_c, P, Y, Y_h, Y_c, /*noalloc=*/true);
 }
 
 extern "C" rnn_status rnn_workspace_check(const rnn_plan *p, void *hip_stream, const void *workspace)
