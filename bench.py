@@ -52,6 +52,8 @@ def parse():
                    help="exact mode: k-ordered unfused products on the VALU (results bit-identical "
                         "to the oracle); reported against the fp32 vector peak")
     p.add_argument("--time-chunk", type=int, default=0, help="steps per time chunk (0: all)")
+    p.add_argument("--exchange", type=int, default=0,
+                   help="H exchange between workgroups: 0 automatic, 1 flags, 2 tagged pairs")
     p.add_argument("--peaks", action="store_true",
                    help="print library references (HBM copy, fp32/bf16 GEMM) and exit")
     p.add_argument("--copy-calibration", action="store_true",
@@ -60,6 +62,11 @@ def parse():
                                                           "COPY_WRITE_DIR"),
                    help="summarise four rocprofv3 --pmc csv runs (FETCH_SIZE / WRITE_SIZE of the "
                         "bench and of --copy-calibration) into per-launch HBM bytes, as JSON")
+    p.add_argument("--stamps", action="store_true",
+                   help="with the instrumented build loaded (RNN_AMD_LIB=recurrent_nn_amd/"
+                        "librecurrent_nn_amd_stamps.so, built by `recurrent_nn_amd/build.py "
+                        "--stamps`): the step loop's cycle stamps of one workgroup "
+                        "(RNN_AMD_STAMP_WG, default 0), median intervals over the steps, as JSON")
     p.add_argument("--counter-summary", metavar="PMC_DIR",
                    help="mean of every counter per dispatch of each kernel in a rocprofv3 --pmc "
                         "csv run, as JSON")
@@ -292,7 +299,8 @@ def cpu_baseline(c, budget_s):
             "threads": nt, **hf, "seconds": dt}
 
 
-def measure(c, steps, warmup, dev, kernel_path=0, exact=False, time_chunk=0, stage_runs=None):
+def measure(c, steps, warmup, dev, kernel_path=0, exact=False, time_chunk=0, stage_runs=None,
+            exchange=0):
     """Run one workload on the GPU: warm-up, exactly `steps` invocations
     between two events on the stream (the timed region), per-stage durations
     from the library's own events over further runs, and each invocation
@@ -307,8 +315,8 @@ def measure(c, steps, warmup, dev, kernel_path=0, exact=False, time_chunk=0, sta
     t = {k: (v.to(dev) if v is not None and k != "sequence_lens" else v)
          for k, v in c.tensors().items()}
     stream = torch.cuda.current_stream(dev)
-    with ra.plan_for_case(c, kernel_path=kernel_path, exact=exact,
-                          time_chunk=time_chunk) as plan:
+    with ra.plan_for_case(c, kernel_path=kernel_path, exact=exact, time_chunk=time_chunk,
+                          exchange=exchange) as plan:
         Y = torch.empty(plan.output_shapes()[0], dtype=torch.float32, device=dev)
         Yh = torch.empty(plan.output_shapes()[1], dtype=torch.float32, device=dev)
         Yc = torch.empty_like(Yh) if c.op == "LSTM" else None
@@ -399,6 +407,72 @@ def rounded(d):
     return d
 
 
+STAMP_SLOTS, STAMP_EVENTS = 1024, 8       # recurrent_nn_amd/csrc/common.h
+
+
+def step_stamps(c, dev, kernel_path=0, exchange=0):
+    """Cycle stamps of the instrumented build: for the two-half kernel each
+    slot is a half-step (events: 0 half start, 1 product start after the flag
+    wait and the first loads, 2 products issued, 3 partial tiles visible after
+    the barrier, 4 gate arithmetic and stores issued, 5 this half's flag
+    stored, from inside the next product); for the four-wave kernel each slot
+    is a phase (0 start, 1 products issued, 2 partial tiles visible, 3 gate
+    arithmetic and stores issued, 4 next phase's flags seen)."""
+    import numpy as np
+    import torch
+
+    import recurrent_nn_amd as ra
+
+    t = {k: (v.to(dev) if v is not None and k != "sequence_lens" else v)
+         for k, v in c.tensors().items()}
+    with ra.plan_for_case(c, kernel_path=kernel_path, exchange=exchange) as plan:
+        desc = dict(kv.split("=", 1) for kv in plan.describe().split() if "=" in kv)
+        off = int(desc.get("stamps", "0"))
+        if not off:
+            raise SystemExit("--stamps needs the instrumented library (RNN_AMD_LIB=..._stamps.so)")
+        nb = STAMP_SLOTS * STAMP_EVENTS * 8
+        args = (t["X"], t["W"], t["R"], t["B"], t["sequence_lens"], t["initial_h"],
+                t["initial_c"], t["P"])
+        for _ in range(2):
+            plan.run(*args)
+        torch.cuda.synchronize()
+        ws = plan.workspace(dev)
+        ws[off:off + nb].zero_()
+        plan.enable_timing(True)
+        plan.run(*args)
+        torch.cuda.synchronize()
+        rec_ms = plan.last_timings()["recurrence"]
+        st = ws[off:off + nb].cpu().numpy().view(np.uint64).reshape(STAMP_SLOTS, STAMP_EVENTS)
+        st = st.astype(np.int64)
+        halves = desc["halves"] == "2"
+        per_step = 2 if halves else int(desc["phases"])
+        n = min(STAMP_SLOTS, c.seq * per_step)
+        lo, hi = 2 * per_step, n - 2 * per_step          # steady slots
+        rows = st[lo:hi]
+        nxt = st[lo + 1:hi + 1, 0]
+        names = (["wait_and_first_loads", "product", "partials_barrier", "gates_and_stores",
+                  "to_next_half"] if halves else
+                 ["product", "partials_barrier", "gates_and_stores", "handover_wait"])
+        if halves:
+            iv = [rows[:, 1] - rows[:, 0], rows[:, 2] - rows[:, 1], rows[:, 3] - rows[:, 2],
+                  rows[:, 4] - rows[:, 3], nxt - rows[:, 4]]
+            flag = rows[:, 5] - rows[:, 4]
+        else:
+            iv = [rows[:, 1] - rows[:, 0], rows[:, 2] - rows[:, 1], rows[:, 3] - rows[:, 2],
+                  rows[:, 4] - rows[:, 3]]
+        period = nxt - rows[:, 0]
+        out = {"workload": c.name, "plan": plan.describe(), "workgroup": int(os.environ.get(
+                   "RNN_AMD_STAMP_WG", "0")), "slot": "half-step" if halves else "phase",
+               "slots_used": int(hi - lo), "recurrence_ms": rec_ms,
+               "us_per_slot": rec_ms * 1e3 / (c.seq * per_step),
+               "median_cycles": {k: float(np.median(v)) for k, v in zip(names, iv)},
+               "median_period_cycles": float(np.median(period))}
+        if halves:
+            out["median_cycles"]["gates_done_to_flag_stored"] = float(np.median(flag))
+        out["cycles_per_us"] = out["median_period_cycles"] / out["us_per_slot"]
+    return out
+
+
 # The five workloads of the operator's benchmark list; the first is timed as
 # the headline line, the others are reported under "configs".
 CONFIGS = ["lstm_bidir_s512_b64_i1024_h1024", "rnn_fwd_s4_b2_i3_h5", "lstm_bidir_s16_b4_i32_h64",
@@ -433,12 +507,17 @@ def main():
         achievable_peaks()
         return
     ra._lib.load()
+    if args.stamps:
+        torch.cuda.set_device(0)
+        print(json.dumps(step_stamps(workloads.workload(args.workload), torch.device("cuda:0"),
+                                     args.kernel_path, args.exchange)), flush=True)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     c = workloads.workload(args.workload)
     print(f"[bench] workload {c.name}: inputs drawn", file=sys.stderr, flush=True)
     m = measure(c, args.steps, args.warmup, dev, kernel_path=args.kernel_path, exact=args.exact,
-                time_chunk=args.time_chunk)
+                time_chunk=args.time_chunk, exchange=args.exchange)
     print(f"[bench] stage ms: {json.dumps(m['stage_ms'])}", file=sys.stderr, flush=True)
     kernels = kernel_figures(c, m, exact=args.exact)
     # size-derived rates of the step loop's operand streams (sizes over the
@@ -447,7 +526,8 @@ def main():
     desc = dict(kv.split("=", 1) for kv in m["plan"].split() if "=" in kv)
     t_step = m["stage_ms"]["recurrence"] * 1e-3 / c.seq
     r_bytes = 4.0 * c.dirs * c.gates * c.hidden * c.hidden
-    h_bytes = 4.0 * int(desc["workgroups"]) * int(desc["BT"]) * int(desc["Hp"])
+    h_elem = 8.0 if desc.get("tagged") == "1" else 4.0      # (value, tag) pairs
+    h_bytes = h_elem * int(desc["workgroups"]) * int(desc["BT"]) * int(desc["Hp"])
     kernels["recurrence"]["size_derived"] = {
         "note": "operand bytes per step divided by the step time; not counter readings",
         "r_bytes_per_step": r_bytes, "r_gbs": r_bytes / t_step / 1e9,
@@ -482,7 +562,7 @@ def main():
     }
     del c
     # ---- the other workloads of the list, same protocol, fewer runs ---------
-    if not args.no_configs and not args.exact and not args.time_chunk:
+    if not args.no_configs and not args.exact and not args.time_chunk and not args.exchange:
         confs = {}
         for name in CONFIGS:
             if name == args.workload:

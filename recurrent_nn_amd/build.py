@@ -42,14 +42,14 @@ HIP_UNITS = ([(f, [], f + ".o") for f in sorted(os.listdir(CSRC))
 CXX_UNITS = [("plan.cpp", [], "plan.cpp.o")]
 
 
-def _compile(unit, verbose):
+def _compile(unit, verbose, build_dir=BUILD, defs=()):
     src, extra, oname = unit
-    obj = os.path.join(BUILD, oname)
+    obj = os.path.join(build_dir, oname)
     path = os.path.join(CSRC, src)
     if unit in CXX_UNITS:
-        cmd = ["g++", *COMMON, *extra, "-c", path, "-o", obj]
+        cmd = ["g++", *COMMON, *defs, *extra, "-c", path, "-o", obj]
     else:
-        cmd = [HIPCC, *COMMON, *HIP_FLAGS, *extra, "-x", "hip", "-c", path, "-o", obj]
+        cmd = [HIPCC, *COMMON, *HIP_FLAGS, *defs, *extra, "-x", "hip", "-c", path, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -58,21 +58,29 @@ def _compile(unit, verbose):
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+# The instrumented build (cycle stamps of one workgroup's steps, read back by
+# `bench.py --stamps`): the same sources with -DRNN_STAMPS, its own objects
+# and library file.  Never loaded unless RNN_AMD_LIB names it.
+STAMPS_BUILD = os.path.join(ROOT, "_build", "recurrent_nn_amd_stamps")
+STAMPS_LIB = os.path.join(HERE, "librecurrent_nn_amd_stamps.so")
+
+
+def build(verbose: bool = False, jobs: int = 8, stamps: bool = False) -> str:
+    build_dir, lib, defs = (STAMPS_BUILD, STAMPS_LIB, ["-DRNN_STAMPS"]) if stamps else (BUILD, LIB, [])
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda u: _compile(u, verbose), HIP_UNITS + CXX_UNITS))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda u: _compile(u, verbose, build_dir, defs), HIP_UNITS + CXX_UNITS))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    t = build(verbose="-v" in sys.argv)
+    t = build(verbose="-v" in sys.argv, stamps="--stamps" in sys.argv)
     print(t)

@@ -46,8 +46,15 @@ struct Layout {
                         // position (rows by decreasing length)
     size_t bar = 0;     // uint32 step flags [D*NBB][2][NUB], then int32 error word
     size_t cellb = 0;   // rnn_cell_run: summed biases expanded to [D][Wb = sum, Rb = 0]
+    size_t stamps = 0;  // instrumented build only: cycle stamps [kStampSlots][kStampEvents]
     size_t total = 0;
 };
+
+// Cycle stamps of the instrumented build (-DRNN_STAMPS): one workgroup's
+// wave 0 records the shader clock at fixed points of each step (phase or
+// half-step) into the workspace; the normal build records nothing.
+constexpr int kStampSlots = 1024;
+constexpr int kStampEvents = 8;
 
 }  // namespace rnnamd
 
@@ -67,6 +74,7 @@ struct rnn_plan {
     int32_t kernel_path = 0;
     uint32_t spin_limit = 0;  // polls before a step barrier gives up
     int32_t withhold_flags = 0;   // test fault injection: step flags are never stored
+    int32_t stamp_wg = 0;     // instrumented build: the workgroup whose steps are stamped
     int64_t S = 0, Bt = 0, I = 0, H = 0;
     int64_t C = 0;            // steps per chunk (time_chunk; S when not chunked)
     rnnamd::ActSpec act[2][3] = {};
@@ -86,6 +94,7 @@ struct rnn_plan {
     int32_t KB = 1;           // 16-wide k blocks per wave (Hp / (16 * NW))
     int32_t resident = 0;     // R slice held in registers across steps
     int32_t halves = 1;       // 2: each step as two half-batch sub-steps (rec_pipe_kernel)
+    int32_t tagged = 0;       // H exchanged as (value, step) pairs, no flags (rec_pipe_kernel)
     int32_t exact = 0;        // exact mode: k-ordered unfused products, exact activations
     int64_t Btp = 16;         // NBB * BT
     int32_t n_wg = 1;         // D * NBB * NUB
@@ -147,6 +156,8 @@ struct InitArgs {
     int64_t n_bar;
     int64_t D, Bt, Btp, H, Hp;
     int32_t layout;
+    int32_t tagged;             // hbuf holds (value, tag) pairs: plane 0 gets tag 1, the
+    int64_t ring_planes;        //   other ring_planes - 1 planes are zeroed (tag 0)
 };
 int launch_init(const InitArgs &a, void *stream);
 
@@ -186,6 +197,7 @@ struct RecArgs {
     int32_t Hp, KB, NW, U, NUB, BT, NBB, MT, NTA, NTB, NT, phases;
     int32_t Btp;
     int32_t halves;         // 1, or 2 half-batch sub-steps per step (rec_pipe_kernel)
+    int32_t tagged;         // H planes hold (value, tag) pairs (rec_pipe_kernel)
     int32_t exact;          // exact mode (rec_exact_kernel)
     int32_t reverse_only, layout, clip_on, input_forget, lbr;
     float clip;
@@ -205,6 +217,9 @@ struct RecArgs {
     int32_t withhold_flags;  // test fault injection: never store the step flags
     // launch range in phase units (step j, phase p) -> q = j * phases + p
     int32_t q_begin, q_end;
+    // instrumented build: stamps[slot][event] of workgroup stamp_wg
+    uint64_t *stamps;
+    int32_t stamp_wg;
     // time chunk of xw_steps steps starting at j_base: XW row = j - j_base;
     // the H history is a ring of xw_steps + 1 planes (plane j mod (steps+1)),
     // r (.) H_prev a ring of xw_steps planes, so one chunk's last plane is the

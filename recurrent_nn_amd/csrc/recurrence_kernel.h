@@ -49,6 +49,20 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Cycle stamps (instrumented build only, -DRNN_STAMPS): thread 0 of workgroup
+// a.stamp_wg stores the shader clock for event e of slot `slot` (a phase or a
+// half-step of the launch).  Compiled out otherwise.
+#ifdef RNN_STAMPS
+#define RNN_STAMP(slot, e)                                                                        \
+    do {                                                                                         \
+        if ((int)blockIdx.x == a.stamp_wg && threadIdx.x == 0 && (slot) >= 0 &&                  \
+            (slot) < kStampSlots)                                                                \
+            a.stamps[(size_t)(slot) * kStampEvents + (e)] = __builtin_amdgcn_s_memtime();        \
+    } while (0)
+#else
+#define RNN_STAMP(slot, e) do { } while (0)
+#endif
+
 // Agent-coherent store (write-through to the device coherence point, no
 // dirty line left in this XCD's L2): how H and r (.) H_prev are published.
 __device__ __forceinline__ void store_coherent(float *p, float v)
@@ -518,6 +532,7 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
     }
     bool dead = false;
     for (int q = a.q_begin; q < a.q_end; ++q) {
+        RNN_STAMP(q - a.q_begin, 0);
         const int j = q / PH;
         const int ph = q - j * PH;
         const int t0 = ph == 0 ? 0 : a.NTA;              // this phase's column tiles
@@ -569,6 +584,7 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
             else if constexpr (TA > 0)
                 product_stream<MT, NT, TA, NT>(acc, asrc, rfrag, Hp, KB, mt_act, prefetch_xw);
         }
+        RNN_STAMP(q - a.q_begin, 1);
         // ---- partial tiles -> LDS, summed in wave order ----------------------
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -581,6 +597,7 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
                     red[(w * BT + mt * 16 + 4 * lq + r) * LDR + nt * 16 + lr] = acc[mt][nt][r];
             }
         __syncthreads();
+        RNN_STAMP(q - a.q_begin, 2);
         auto rec_at = [&](int rl, int col) {
             const float *p = red + rl * LDR + col;
             float v = p[0];
@@ -676,12 +693,14 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
             for (int e = tid; e < rows * padw; e += kThreads)
                 store_coherent(pl + (size_t)(e / padw) * Hp + a.H + e % padw, 0.0f);
         }
+        RNN_STAMP(q - a.q_begin, 3);
         if (q + 1 < a.q_end)
             group_publish_wait(a.bar + (size_t)grp * 2 * a.NUB, ub, (uint32_t)(q + 1), wub_lo,
                                wub_hi - wub_lo + 1, a.err, a.spin_limit, a.withhold_flags != 0,
                                dead);
         else
             __syncthreads();
+        RNN_STAMP(q - a.q_begin, 4);
     }
 
     // ---- end of this launch: keep or publish the states ---------------------

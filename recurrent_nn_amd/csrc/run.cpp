@@ -68,6 +68,7 @@ RecArgs rec_args(const rnn_plan &p, unsigned char *ws, const float *B, const flo
     r.phases = p.phases;
     r.Btp = (int32_t)p.Btp;
     r.halves = p.halves;
+    r.tagged = p.tagged;
     r.exact = p.exact;
     r.reverse_only = p.reverse_only;
     r.layout = p.layout;
@@ -94,6 +95,8 @@ RecArgs rec_args(const rnn_plan &p, unsigned char *ws, const float *B, const flo
     r.withhold_flags = p.withhold_flags;
     r.q_begin = 0;
     r.q_end = (int32_t)(p.S * p.phases);
+    r.stamps = p.ws.stamps ? (uint64_t *)(ws + p.ws.stamps) : nullptr;
+    r.stamp_wg = p.stamp_wg;
     r.j_base = 0;
     r.xw_steps = (int32_t)p.C;
     return r;
@@ -316,6 +319,8 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
     ia.H = p->H;
     ia.Hp = p->Hp;
     ia.layout = p->layout;
+    ia.tagged = p->tagged;
+    ia.ring_planes = p->C + 1;
     int rc = launch_init(ia, s);
     if (rc)
         return hip_fail((hipError_t)rc, "state init");
