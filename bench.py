@@ -52,8 +52,6 @@ def parse():
                    help="exact mode: k-ordered unfused products on the VALU (results bit-identical "
                         "to the oracle); reported against the fp32 vector peak")
     p.add_argument("--time-chunk", type=int, default=0, help="steps per time chunk (0: all)")
-    p.add_argument("--exchange", type=int, default=0,
-                   help="H exchange between workgroups: 0 automatic, 1 flags, 2 tagged pairs")
     p.add_argument("--peaks", action="store_true",
                    help="print library references (HBM copy, fp32/bf16 GEMM) and exit")
     p.add_argument("--copy-calibration", action="store_true",
@@ -299,8 +297,7 @@ def cpu_baseline(c, budget_s):
             "threads": nt, **hf, "seconds": dt}
 
 
-def measure(c, steps, warmup, dev, kernel_path=0, exact=False, time_chunk=0, stage_runs=None,
-            exchange=0):
+def measure(c, steps, warmup, dev, kernel_path=0, exact=False, time_chunk=0, stage_runs=None):
     """Run one workload on the GPU: warm-up, exactly `steps` invocations
     between two events on the stream (the timed region), per-stage durations
     from the library's own events over further runs, and each invocation
@@ -315,8 +312,7 @@ def measure(c, steps, warmup, dev, kernel_path=0, exact=False, time_chunk=0, sta
     t = {k: (v.to(dev) if v is not None and k != "sequence_lens" else v)
          for k, v in c.tensors().items()}
     stream = torch.cuda.current_stream(dev)
-    with ra.plan_for_case(c, kernel_path=kernel_path, exact=exact, time_chunk=time_chunk,
-                          exchange=exchange) as plan:
+    with ra.plan_for_case(c, kernel_path=kernel_path, exact=exact, time_chunk=time_chunk) as plan:
         Y = torch.empty(plan.output_shapes()[0], dtype=torch.float32, device=dev)
         Yh = torch.empty(plan.output_shapes()[1], dtype=torch.float32, device=dev)
         Yc = torch.empty_like(Yh) if c.op == "LSTM" else None
@@ -410,7 +406,7 @@ def rounded(d):
 STAMP_SLOTS, STAMP_EVENTS = 1024, 8       # recurrent_nn_amd/csrc/common.h
 
 
-def step_stamps(c, dev, kernel_path=0, exchange=0):
+def step_stamps(c, dev, kernel_path=0):
     """Cycle stamps of the instrumented build: for the two-half kernel each
     slot is a half-step (events: 0 half start, 1 product start after the flag
     wait and the first loads, 2 products issued, 3 partial tiles visible after
@@ -425,7 +421,7 @@ def step_stamps(c, dev, kernel_path=0, exchange=0):
 
     t = {k: (v.to(dev) if v is not None and k != "sequence_lens" else v)
          for k, v in c.tensors().items()}
-    with ra.plan_for_case(c, kernel_path=kernel_path, exchange=exchange) as plan:
+    with ra.plan_for_case(c, kernel_path=kernel_path) as plan:
         desc = dict(kv.split("=", 1) for kv in plan.describe().split() if "=" in kv)
         off = int(desc.get("stamps", "0"))
         if not off:
@@ -510,14 +506,14 @@ def main():
     if args.stamps:
         torch.cuda.set_device(0)
         print(json.dumps(step_stamps(workloads.workload(args.workload), torch.device("cuda:0"),
-                                     args.kernel_path, args.exchange)), flush=True)
+                                     args.kernel_path)), flush=True)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     c = workloads.workload(args.workload)
     print(f"[bench] workload {c.name}: inputs drawn", file=sys.stderr, flush=True)
     m = measure(c, args.steps, args.warmup, dev, kernel_path=args.kernel_path, exact=args.exact,
-                time_chunk=args.time_chunk, exchange=args.exchange)
+                time_chunk=args.time_chunk)
     print(f"[bench] stage ms: {json.dumps(m['stage_ms'])}", file=sys.stderr, flush=True)
     kernels = kernel_figures(c, m, exact=args.exact)
     # size-derived rates of the step loop's operand streams (sizes over the
@@ -526,8 +522,7 @@ def main():
     desc = dict(kv.split("=", 1) for kv in m["plan"].split() if "=" in kv)
     t_step = m["stage_ms"]["recurrence"] * 1e-3 / c.seq
     r_bytes = 4.0 * c.dirs * c.gates * c.hidden * c.hidden
-    h_elem = 8.0 if desc.get("tagged") == "1" else 4.0      # (value, tag) pairs
-    h_bytes = h_elem * int(desc["workgroups"]) * int(desc["BT"]) * int(desc["Hp"])
+    h_bytes = 4.0 * int(desc["workgroups"]) * int(desc["BT"]) * int(desc["Hp"])
     kernels["recurrence"]["size_derived"] = {
         "note": "operand bytes per step divided by the step time; not counter readings",
         "r_bytes_per_step": r_bytes, "r_gbs": r_bytes / t_step / 1e9,
@@ -562,7 +557,7 @@ def main():
     }
     del c
     # ---- the other workloads of the list, same protocol, fewer runs ---------
-    if not args.no_configs and not args.exact and not args.time_chunk and not args.exchange:
+    if not args.no_configs and not args.exact and not args.time_chunk:
         confs = {}
         for name in CONFIGS:
             if name == args.workload:

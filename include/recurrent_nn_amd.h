@@ -123,15 +123,6 @@ typedef struct rnn_attrs {
                                           binary64 method; results do not depend on the
                                           tiling and match that definition bit for bit.
                                           0 = fast mode (matrix-core products).           */
-    int32_t exchange;                  /* how H passes between workgroups each step:
-                                          0 = automatic; 1 = plain values, each workgroup
-                                          publishing a flag once its stores are complete;
-                                          2 = tagged: every value stored with its step
-                                          number in one 8-byte write, checked by the
-                                          readers (no flags; for steps with little work
-                                          per workgroup).  Tagged needs the two-half form
-                                          (batch_halves) and fast mode; else InvalidInput.
-                                          Results are identical either way.              */
 } rnn_attrs;
 
 /* Dimensions: hidden is R's last dimension, num_directions W's first. */
@@ -268,9 +259,8 @@ rnn_status rnn_run_noalloc(rnn_plan *plan, void *hip_stream, const float *X, con
  * timed out).  RNN_OK when clean, RNN_ERR_DEVICE otherwise.  For tests of
  * this path, a plan created while the environment variable
  * RNN_AMD_TEST_WITHHOLD_FLAGS is set to a non-zero value never stores its
- * step flags (with the tagged exchange: stores every H value with a tag no
- * reader expects), so every wait between steps runs out barrier_spin_limit
- * (results are then undefined, and the kernel still finishes).
+ * step flags, so every wait between steps runs out barrier_spin_limit (results
+ * are then undefined, and the kernel still finishes).
  */
 rnn_status rnn_workspace_check(const rnn_plan *plan, void *hip_stream, const void *workspace);
 

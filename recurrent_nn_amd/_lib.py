@@ -56,7 +56,6 @@ class rnn_attrs(ctypes.Structure):
         ("batch_halves", ctypes.c_int32),
         ("time_chunk", ctypes.c_int32),
         ("exact", ctypes.c_int32),
-        ("exchange", ctypes.c_int32),
     ]
 
 

@@ -94,7 +94,6 @@ struct rnn_plan {
     int32_t KB = 1;           // 16-wide k blocks per wave (Hp / (16 * NW))
     int32_t resident = 0;     // R slice held in registers across steps
     int32_t halves = 1;       // 2: each step as two half-batch sub-steps (rec_pipe_kernel)
-    int32_t tagged = 0;       // H exchanged as (value, step) pairs, no flags (rec_pipe_kernel)
     int32_t exact = 0;        // exact mode: k-ordered unfused products, exact activations
     int64_t Btp = 16;         // NBB * BT
     int32_t n_wg = 1;         // D * NBB * NUB
@@ -156,8 +155,6 @@ struct InitArgs {
     int64_t n_bar;
     int64_t D, Bt, Btp, H, Hp;
     int32_t layout;
-    int32_t tagged;             // hbuf holds (value, tag) pairs: plane 0 gets tag 1, the
-    int64_t ring_planes;        //   other ring_planes - 1 planes are zeroed (tag 0)
 };
 int launch_init(const InitArgs &a, void *stream);
 
@@ -197,7 +194,6 @@ struct RecArgs {
     int32_t Hp, KB, NW, U, NUB, BT, NBB, MT, NTA, NTB, NT, phases;
     int32_t Btp;
     int32_t halves;         // 1, or 2 half-batch sub-steps per step (rec_pipe_kernel)
-    int32_t tagged;         // H planes hold (value, tag) pairs (rec_pipe_kernel)
     int32_t exact;          // exact mode (rec_exact_kernel)
     int32_t reverse_only, layout, clip_on, input_forget, lbr;
     float clip;

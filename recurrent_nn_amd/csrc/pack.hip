@@ -127,11 +127,6 @@ __global__ void init_kernel(InitArgs a)
     const int64_t plane = a.D * a.Btp * a.Hp;
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    // tagged pairs: the planes after the first start with tag 0, which no
-    // step ever expects (the plane of H before step j carries tag j + 1)
-    if (a.tagged)
-        for (int64_t i = plane + tid; i < a.ring_planes * plane; i += stride)
-            ((uint64_t *)a.hbuf)[i] = 0ull;
     for (int64_t i = tid; i < plane; i += stride) {
         float v = 0.0f;
         if (a.h0) {
@@ -143,10 +138,7 @@ __global__ void init_kernel(InitArgs a)
                 v = a.layout == 0 ? a.h0[(d * a.Bt + b) * a.H + k] : a.h0[(b * a.D + d) * a.H + k];
             }
         }
-        if (a.tagged)      // H before step 0: tag 1
-            ((uint64_t *)a.hbuf)[i] = (1ull << 32) | (uint64_t)__float_as_uint(v);
-        else
-            a.hbuf[i] = v;
+        a.hbuf[i] = v;
     }
     if (a.cbuf) {
         const int64_t n = a.D * a.Bt * a.H;
@@ -171,7 +163,7 @@ __global__ void init_kernel(InitArgs a)
 
 int launch_init(const InitArgs &a, void *stream)
 {
-    const int64_t work = a.D * a.Btp * a.Hp * (a.tagged ? a.ring_planes : 1);
+    const int64_t work = a.D * a.Btp * a.Hp;
     int64_t blocks = (work + 255) / 256;
     if (blocks > 4096)
         blocks = 4096;

@@ -270,23 +270,6 @@ rnn_status choose_tiling(const rnn_attrs &a, rnn_plan &p)
         return RNN_ERR_INVALID_INPUT;
     }
     p.halves = (halves_ok && a.batch_halves != 1) ? 2 : 1;
-    // H exchange: flags unless tagged pairs are asked for.  (Measured on the
-    // GRU of hidden 512, batch 32: tagged 5.66 us/step against 4.69 with
-    // flags -- the waves that store H wait for those stores' write-through
-    // before any later load either way, and the tagged form adds 8-byte
-    // values and agent-scope loads.)
-    if (a.exchange < 0 || a.exchange > 2) {
-        set_error("exchange must be 0, 1 or 2");
-        return RNN_ERR_INVALID_INPUT;
-    }
-    const bool ring_fits = (double)(p.C + 1) * p.D * p.Btp * p.Hp * 8.0 < 2147483648.0;
-    const bool tag_ok = p.halves == 2 && !p.exact && ring_fits;
-    if (a.exchange == 2 && !tag_ok) {
-        set_error("exchange = 2 (tagged) needs the two-half step loop, fast mode and an H history "
-                  "under 2 GiB");
-        return RNN_ERR_INVALID_INPUT;
-    }
-    p.tagged = a.exchange == 2;
     if (p.exact) {
         p.halves = 1;                              // the exact kernel has one form
         if (a.batch_halves == 2) {
@@ -316,7 +299,7 @@ void make_layout(rnn_plan &p)
     L.rp = take((size_t)p.D * p.NUB * p.NT * 16 * p.Hp * 4);
     L.xb = take(p.proj_bf16 ? (size_t)p.D * p.C * p.Bt * p.I * 2 : 0);
     L.xw = take((size_t)p.D * p.C * p.Bt * GH * 4);
-    L.hbuf = take((size_t)(p.C + 1) * p.D * p.Btp * p.Hp * (p.tagged ? 8 : 4));
+    L.hbuf = take((size_t)(p.C + 1) * p.D * p.Btp * p.Hp * 4);
     L.sbuf = take(p.phases == 2 ? (size_t)p.C * p.D * p.Btp * p.Hp * 4 : 0);
     L.cbuf = take(p.op == RNN_OP_LSTM ? (size_t)p.D * p.Bt * p.H * 4 : 0);
     L.zbuf = take(p.phases == 2 ? (size_t)p.D * p.Bt * p.H * 4 : 0);
@@ -470,11 +453,11 @@ extern "C" rnn_status rnn_plan_describe(const rnn_plan *p, char *buf, size_t len
     std::snprintf(buf, len,
                   "op=%d G=%d D=%d S=%lld C=%lld Bt=%lld I=%lld H=%lld U=%d NUB=%d BT=%d NBB=%d "
                   "MT=%d NTA=%d NTB=%d phases=%d Hp=%lld waves=%d KB=%d resident=%d halves=%d "
-                  "tagged=%d exact=%d workgroups=%d path=%d persist=%d ws=%zu stamps=%zu",
+                  "exact=%d workgroups=%d path=%d persist=%d ws=%zu stamps=%zu",
                   p->op, p->G, p->D, (long long)p->S, (long long)p->C, (long long)p->Bt,
                   (long long)p->I,
                   (long long)p->H, p->U, p->NUB, p->BT, p->NBB, p->MT, p->NTA, p->NTB, p->phases,
-                  (long long)p->Hp, p->NW, p->KB, p->resident, p->halves, p->tagged, p->exact, p->n_wg,
+                  (long long)p->Hp, p->NW, p->KB, p->resident, p->halves, p->exact, p->n_wg,
                   p->kernel_path,
                   p->can_persist, p->ws.total, p->ws.stamps);
     return RNN_OK;

@@ -14,7 +14,7 @@ namespace rnnamd {
     rec_fn rec_get_resident_a##A(int nw, int mt, int nt, int kb, int ta);                         \
     rec_fn rec_get_streamed2_a##A(int mt, int nt, int ta);                                        \
     rec_fn rec_get_streamed8_a##A(int mt, int nt, int ta);                                        \
-    rec_fn rec_get_pipe_a##A(int mth, int nt, int kb, int p, int tagged);
+    rec_fn rec_get_pipe_a##A(int mth, int nt, int kb, int p);
 RNN_DECL(0)
 RNN_DECL(1)
 RNN_DECL(2)
@@ -67,14 +67,14 @@ static rec_fn get_streamed(int act, int p, int mt, int nt, int ta)
     }
 }
 
-static rec_fn get_pipe(int act, int mth, int nt, int kb, int p, int tg)
+static rec_fn get_pipe(int act, int mth, int nt, int kb, int p)
 {
     switch (act) {
-    case 1: return rec_get_pipe_a1(mth, nt, kb, p, tg);
-    case 2: return rec_get_pipe_a2(mth, nt, kb, p, tg);
-    case 3: return rec_get_pipe_a3(mth, nt, kb, p, tg);
-    case 4: return rec_get_pipe_a4(mth, nt, kb, p, tg);
-    default: return rec_get_pipe_a0(mth, nt, kb, p, tg);
+    case 1: return rec_get_pipe_a1(mth, nt, kb, p);
+    case 2: return rec_get_pipe_a2(mth, nt, kb, p);
+    case 3: return rec_get_pipe_a3(mth, nt, kb, p);
+    case 4: return rec_get_pipe_a4(mth, nt, kb, p);
+    default: return rec_get_pipe_a0(mth, nt, kb, p);
     }
 }
 
@@ -98,9 +98,7 @@ static rec_fn pick(const RecArgs &a, int resident)
         // phase, at most two pairs per thread and half
         const bool ok = resident && a.NW == 4 && a.phases == 1 && a.MT % 2 == 0 &&
                         (a.BT / 2) * a.U <= 2 * 256;
-        return ok ? get_pipe(act_set(a), a.MT / 2, a.NT, a.KB, ((a.BT / 2) * a.U + 255) / 256,
-                             a.tagged)
-                  : nullptr;
+        return ok ? get_pipe(act_set(a), a.MT / 2, a.NT, a.KB, ((a.BT / 2) * a.U + 255) / 256) : nullptr;
     }
     const int nthr = 64 * a.NW;
     const int np = (a.BT * a.U + nthr - 1) / nthr;

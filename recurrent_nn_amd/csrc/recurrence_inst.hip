@@ -86,18 +86,13 @@ rec_fn RNN_CAT(RNN_NAME, RNN_ACT)(int mt, int nt, int ta)
 #elif RNN_FAMILY == 3
 // Two half-batch sub-steps: mth 16-row tiles per half (BT = 32 * mth), nt
 // 16-column tiles, kb 16-k blocks per wave (R slice of nt * kb * 4 registers
-// per lane), p pairs per thread and half (1 or 2), H exchanged behind flags
-// or as tagged pairs.
-rec_fn RNN_CAT(rec_get_pipe_a, RNN_ACT)(int mth, int nt, int kb, int p, int tagged)
+// per lane), p pairs per thread and half (1 or 2).
+rec_fn RNN_CAT(rec_get_pipe_a, RNN_ACT)(int mth, int nt, int kb, int p)
 {
 #define RNN_P2(MTH_, NT_, KB_)                                                                    \
-    if (mth == MTH_ && nt == NT_ && kb == KB_) {                                                 \
-        if (tagged)                                                                              \
-            return p == 1 ? rec_pipe_kernel<MTH_, NT_, KB_, RNN_ACT, 1, true>                    \
-                          : rec_pipe_kernel<MTH_, NT_, KB_, RNN_ACT, 2, true>;                   \
-        return p == 1 ? rec_pipe_kernel<MTH_, NT_, KB_, RNN_ACT, 1, false>                       \
-                      : rec_pipe_kernel<MTH_, NT_, KB_, RNN_ACT, 2, false>;                      \
-    }
+    if (mth == MTH_ && nt == NT_ && kb == KB_)                                                   \
+        return p == 1 ? rec_pipe_kernel<MTH_, NT_, KB_, RNN_ACT, 1>                              \
+                      : rec_pipe_kernel<MTH_, NT_, KB_, RNN_ACT, 2>;
     RNN_P2(1, 1, 8)
     RNN_P2(1, 1, 16)
     RNN_P2(1, 2, 8)

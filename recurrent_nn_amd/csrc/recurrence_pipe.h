@@ -85,168 +85,6 @@ __device__ __forceinline__ void product_res_hooked(f4 (&acc)[MT][NT],
     }
 }
 
-// ---- tagged exchange ------------------------------------------------------
-// For steps too short to hide a flag hand-over (a few MFMAs per wave), H is
-// exchanged without flags: every element of an H plane is stored together
-// with the number of the step it belongs to, as one 8-byte (value, tag) pair
-// written through to the device coherence point, and a reader checks the
-// tag of every value it uses.  The plane holding H before step j carries tag
-// j + 1; the ring of planes starts each run zeroed (tag 0 is never valid),
-// and tags are absolute step numbers, so a plane reused by a later chunk
-// never passes for a newer one.  A value is trusted only with its tag: a
-// first, ordinary load may come from a cache line fetched before the writer
-// stored it, so any lane whose tags differ loads those pairs again at agent
-// scope (from the coherence point, not from a cache) until they match, or
-// until spin_limit polls have passed (then the error word is raised and the
-// kernel runs on; its results are undefined).
-
-// One lane's four consecutive k values of one row, as (value, tag) pairs.
-struct Tagged4 {
-    uint4 lo, hi;
-};
-
-// Loads through a buffer resource over the H history at agent scope (cache
-// policy 16, sc1): from the device coherence point, never from a cache line
-// fetched before the writer stored it.
-constexpr int kLoadAgent = 16;
-
-template <int POL>
-__device__ __forceinline__ Tagged4 load_tagged4(__amdgpu_buffer_rsrc_t rs, uint32_t off)
-{
-    Tagged4 t;
-    t.lo = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, POL));
-    t.hi = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, POL));
-    return t;
-}
-
-__device__ __forceinline__ bool tags_are(const Tagged4 &t, uint32_t tag)
-{
-    return t.lo.y == tag && t.lo.w == tag && t.hi.y == tag && t.hi.w == tag;
-}
-
-// The four values of t once every tag is `tag`: a lane whose tags differ
-// loads its pairs again at agent scope until they match or spin_limit polls
-// have passed (then the error word is raised and the values are undefined).
-__device__ __forceinline__ f4 take_tagged4(Tagged4 t, __amdgpu_buffer_rsrc_t rs, uint32_t off,
-                                           uint32_t tag, uint32_t spin_limit, int32_t *err,
-                                           bool &dead)
-{
-    bool ok = tags_are(t, tag);
-    if (!ok) {
-        uint32_t n = 0;
-        while (!ok && !dead) {
-            __builtin_amdgcn_s_sleep(1);
-            t = load_tagged4<kLoadAgent>(rs, off);
-            ok = tags_are(t, tag);
-            if (!ok && ++n > spin_limit) {
-                __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                dead = true;
-            }
-        }
-    }
-    return f4{__uint_as_float(t.lo.x), __uint_as_float(t.lo.z), __uint_as_float(t.hi.x),
-              __uint_as_float(t.hi.z)};
-}
-
-// Write-through store of one (value, tag) pair.
-__device__ __forceinline__ void store_tagged(uint64_t *p, float v, uint32_t tag)
-{
-    __hip_atomic_store(p, ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Depth of the tagged A ring: a half's first blocks (up to 8) are loaded
-// together as soon as the other half's partial tiles are in LDS, validated
-// together at the start of the product and, where any tag is stale, loaded
-// again together -- one round trip per retry, not one per block.
-constexpr int kTagPrefetch = 8;
-
-template <int MT, int KBR, int PD>
-__device__ __forceinline__ void prime_ring_tagged(Tagged4 (&ring)[(PD < KBR ? PD : KBR) + 1][MT],
-                                                  __amdgpu_buffer_rsrc_t rs, uint32_t off, int Hp)
-{
-    constexpr int D_ = PD < KBR ? PD : KBR;
-#pragma unroll
-    for (int p = 0; p < D_; ++p)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            ring[p][mt] = load_tagged4<kLoadAgent>(rs, off + (uint32_t)(mt * 16 * Hp + p * 16) * 8u);
-}
-
-// product_res_hooked with tagged A operands.  The primed blocks are checked
-// first, all together (reloaded together while any tag of a batch row is
-// stale); later blocks are loaded at agent scope during the product and
-// checked one by one.  Row tile mt of this lane holds a batch row only when
-// row0 + 16 * mt < rows: the padding rows of a ragged batch tile are never
-// written, feed only padding output rows, and are used unchecked.
-template <int MT, int NT, int KBR, int PD, typename Mid>
-__device__ __forceinline__ void product_res_tagged(f4 (&acc)[MT][NT],
-                                                   Tagged4 (&ring)[(PD < KBR ? PD : KBR) + 1][MT],
-                                                   __amdgpu_buffer_rsrc_t rs, uint32_t off, int Hp,
-                                                   const f4 (&rr)[NT][KBR], Mid mid, uint32_t tag,
-                                                   int row0, int rows, uint32_t spin_limit,
-                                                   int32_t *err, bool &dead)
-{
-    constexpr int D_ = PD < KBR ? PD : KBR;
-    auto ring_ok = [&]() {
-        bool ok = true;
-#pragma unroll
-        for (int p = 0; p < D_; ++p)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                ok = ok && (row0 + 16 * mt >= rows || tags_are(ring[p][mt], tag));
-        return ok;
-    };
-    bool ok = ring_ok();
-    uint32_t n = 0;
-    while (!ok && !dead) {
-        __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-        for (int p = 0; p < D_; ++p)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                ring[p][mt] = load_tagged4<kLoadAgent>(rs, off + (uint32_t)(mt * 16 * Hp + p * 16) * 8u);
-        ok = ring_ok();
-        if (!ok && ++n > spin_limit) {
-            __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            dead = true;
-        }
-    }
-    if constexpr (D_ >= KBR)
-        mid();
-#pragma unroll
-    for (int kb = 0; kb < KBR; ++kb) {
-        if (kb + D_ < KBR) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                ring[(kb + D_) % (D_ + 1)][mt] = load_tagged4<kLoadAgent>(
-                    rs, off + (uint32_t)(mt * 16 * Hp + (kb + D_) * 16) * 8u);
-            if (kb + D_ == KBR - 1)
-                mid();
-        }
-        f4 av[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const Tagged4 &t = ring[kb % (D_ + 1)][mt];
-            av[mt] = (kb >= D_ && row0 + 16 * mt < rows)
-                         ? take_tagged4(t, rs, off + (uint32_t)(mt * 16 * Hp + kb * 16) * 8u, tag,
-                                        spin_limit, err, dead)
-                         : f4{__uint_as_float(t.lo.x), __uint_as_float(t.lo.z),
-                              __uint_as_float(t.hi.x), __uint_as_float(t.hi.z)};
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt][s], rr[nt][kb][s],
-                                                                       acc[mt][nt], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-}
-
 // LDS bytes: partial tiles of both halves (column-major, BT/2 + 4 rows per
 // column), h and c per pair, lengths, the per-unit constants, two publish
 // counters.
@@ -259,9 +97,7 @@ __host__ __device__ inline size_t rec_pipe_lds_bytes(int bt, int nt, int u)
 // block than the full tile, so more blocks in flight; 3 measured best).
 constexpr int kPipePrefetch = 3;
 
-// TAG: H exchanged as tagged pairs (see "tagged exchange" above) instead of
-// plain values behind per-half flags.
-template <int MTH, int NT, int KBR, int ACT, int P, bool TAG>
+template <int MTH, int NT, int KBR, int ACT, int P>
 __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
 {
     constexpr int BTH = MTH * 16;                // rows per half
@@ -348,8 +184,7 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
         const int j0 = a.q_begin;
         for (int pi = tid; pi < npairs; pi += 256) {
             const int rl = pi / uc, u = pi - rl * uc;
-            const size_t hi = (size_t)(j0 % (a.xw_steps + 1)) * plane + drow + (size_t)rl * Hp + u0 + u;
-            hst[pi] = TAG ? __uint_as_float((uint32_t)((const uint64_t *)a.hbuf)[hi]) : a.hbuf[hi];
+            hst[pi] = a.hbuf[(size_t)(j0 % (a.xw_steps + 1)) * plane + drow + (size_t)rl * Hp + u0 + u];
             cst[pi] = op == RNN_OP_LSTM ? a.cbuf[((size_t)d * a.Bt + row0 + rl) * a.H + u0 + u] : 0.0f;
         }
         for (int rl = tid; rl < rows; rl += 256)
@@ -392,7 +227,10 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
     float hreg[2][P], creg[2][P], kc[2][P][11];
     int lreg[2][P];
     uint32_t hoff[2][P];                         // offset of the pair in an H plane (from drow)
-    size_t xoff[2][P], yoff[2][P];               // offsets of the pair's XW and Y at step 0
+    // XW element offsets fit 32 bits: the scratch limit keeps each
+    // direction's projections under 2^30 floats
+    uint32_t xoff[2][P];
+    size_t yoff[2][P];                           // offset of the pair's Y at step 0
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -408,7 +246,7 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
             for (int e = 0; e < 11; ++e)
                 kc[h][k][e] = cst_u[e * a.U + u];
             hoff[h][k] = (uint32_t)(rl * Hp + gu);
-            xoff[h][k] = xwd + (size_t)(row0 + rl) * GH + u;
+            xoff[h][k] = (uint32_t)(xwd + (size_t)(row0 + rl) * GH + u);
             yoff[h][k] = a.layout == 0 ? ((size_t)d * a.Bt + b) * a.H + gu
                                        : ((size_t)b * a.S * a.D + d) * a.H + gu;
         }
@@ -441,7 +279,7 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
     uint32_t pend_v = 0, pend_gen = 0;
     uint32_t gens[2] = {0u, 0u};
     auto publish = [&]() {
-        if (!TAG && pend_h >= 0) {
+        if (pend_h >= 0) {
             wait_stores();                       // this wave's H stores have completed
             if (lane == 0) {
                 const uint32_t old = __hip_atomic_fetch_add(ctr + pend_h, 1u, __ATOMIC_RELAXED,
@@ -461,37 +299,17 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
     auto a_src = [&](int pl, int h) {
         return a.hbuf + (size_t)pl * plane + drow + (size_t)(h * BTH + lr) * Hp + k0 + 4 * lq;
     };
-    // tagged: the same element index, in bytes of 8-byte pairs, within a
-    // buffer resource over the whole ring (under 4 GiB: the plan checks)
-    uint64_t *hbuf64 = (uint64_t *)a.hbuf;
-    const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)a.hbuf, (short)0, (int)(TAG ? (uint32_t)((size_t)ring_n * plane * 8) : 0u),
-        0x00020000);
-    auto a_off = [&](int pl, int h) {
-        return (uint32_t)(((size_t)pl * plane + drow + (size_t)(h * BTH + lr) * Hp + k0 + 4 * lq) * 8);
-    };
     int pj = a.q_begin % ring_n;                 // plane of step q
     auto next_plane = [&](int pl) { return pl + 1 == ring_n ? 0 : pl + 1; };
     constexpr int RING = (kPipePrefetch < KBR ? kPipePrefetch : KBR) + 1;
-    constexpr int TRING = (kTagPrefetch < KBR ? kTagPrefetch : KBR) + 1;
-    f4 ring[TAG ? 1 : RING][MTH];
-    Tagged4 tring[TAG ? TRING : 1][MTH];
-    (void)tring;
-    if (a.q_begin < a.q_end) {
-        if constexpr (TAG)
-            prime_ring_tagged<MTH, KBR, kTagPrefetch>(tring, hrs, a_off(pj, 0), Hp);
-        else
-            prime_ring<MTH, KBR, kPipePrefetch>(ring, a_src(pj, 0), Hp);
-    }
+    f4 ring[RING][MTH];
+    if (a.q_begin < a.q_end)
+        prime_ring<MTH, KBR, kPipePrefetch>(ring, a_src(pj, 0), Hp);
     bool primed = true;                          // the next product's first blocks are loaded
 
     for (int q = a.q_begin; q < a.q_end; ++q) {
         const int j = q;                         // one phase per step
         const int pj1 = next_plane(pj);
-        // tag of the H this step writes (test fault injection: a tag no
-        // reader expects, so that every wait runs out its spin limit)
-        const uint32_t htag = a.withhold_flags ? 0u : (uint32_t)(j + 2);
-        (void)htag;
         float *hnext = a.hbuf + (size_t)pj1 * plane + drow;   // (+ hoff: the pair)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -504,14 +322,10 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
             const int nq = h == 0 ? q : q + 1, nh = 1 - h;
             const bool has_next = nq < a.q_end;
             if (!primed) {                       // its flags were not all set earlier
-                if constexpr (TAG) {
-                    prime_ring_tagged<MTH, KBR, kTagPrefetch>(tring, hrs, a_off(pj, h), Hp);
-                } else {
-                    if (!dead)
-                        wave_wait_flags(flags0 + (size_t)h * a.NUB + wub_lo, wub_hi - wub_lo + 1,
-                                        (uint32_t)q, a.err, a.spin_limit, dead);
-                    prime_ring<MTH, KBR, kPipePrefetch>(ring, a_src(pj, h), Hp);
-                }
+                if (!dead)
+                    wave_wait_flags(flags0 + (size_t)h * a.NUB + wub_lo, wub_hi - wub_lo + 1,
+                                    (uint32_t)q, a.err, a.spin_limit, dead);
+                prime_ring<MTH, KBR, kPipePrefetch>(ring, a_src(pj, h), Hp);
             }
             RNN_STAMP(slot, 1);
             float xw[P][4];
@@ -549,23 +363,15 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
                 if (EARLY && need_wait && nfl <= 64 && lane < nfl)
                     fv = __hip_atomic_load(nflags + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             };
-            if constexpr (TAG) {
-                // the plane holding H before step j carries tag j + 1
-                product_res_tagged<MTH, NT, KBR, kTagPrefetch>(acc, tring, hrs, a_off(pj, h), Hp,
-                                                                rr, prefetch_xw, (uint32_t)(j + 1),
-                                                                h * BTH + lr, rows, a.spin_limit,
-                                                                a.err, dead);
-            } else {
-                product_res_hooked<MTH, NT, KBR, kPipePrefetch, KH, KP>(
-                    acc, ring, a_src(pj, h), Hp, rr, prefetch_xw,
-                    [&]() {
-                        const bool had = pend_h >= 0;
-                        publish();
-                        if (had)
-                            RNN_STAMP(slot - 1, 5);   // the previous half's flag is out
-                    },
-                    poll_next);
-            }
+            product_res_hooked<MTH, NT, KBR, kPipePrefetch, KH, KP>(
+                acc, ring, a_src(pj, h), Hp, rr, prefetch_xw,
+                [&]() {
+                    const bool had = pend_h >= 0;
+                    publish();
+                    if (had)
+                        RNN_STAMP(slot - 1, 5);   // the previous half's flag is out
+                },
+                poll_next);
             RNN_STAMP(slot, 2);
             // partial tiles, column-major: a lane's four rows of a column are
             // contiguous (one 16-byte store per tile)
@@ -580,21 +386,10 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
             // if they were all set, load the next product's first k blocks now,
             // so that their latency overlaps this half's gate arithmetic;
             // otherwise wait for them only before that product
-            if constexpr (TAG) {
-                // the next half's blocks are loaded now, at agent scope, so
-                // that their round trip overlaps this half's gate arithmetic;
-                // a value not yet written is caught by its tag and loaded
-                // again at the start of that product
-                primed = true;
-                if (has_next)
-                    prime_ring_tagged<MTH, KBR, kTagPrefetch>(tring, hrs,
-                                                              a_off(h == 0 ? pj : pj1, nh), Hp);
-            } else {
-                primed = !need_wait || (EARLY && nfl <= 64 && __all(fv >= (uint32_t)nq));
-                asm volatile("" ::: "memory");
-                if (has_next && primed)
-                    prime_ring<MTH, KBR, kPipePrefetch>(ring, a_src(h == 0 ? pj : pj1, nh), Hp);
-            }
+            primed = !need_wait || (EARLY && nfl <= 64 && __all(fv >= (uint32_t)nq));
+            asm volatile("" ::: "memory");
+            if (has_next && primed)
+                prime_ring<MTH, KBR, kPipePrefetch>(ring, a_src(h == 0 ? pj : pj1, nh), Hp);
 
             // ---- gate arithmetic of this thread's pairs of half h -------------
             // (computed for every pair and kept only while the row is active,
@@ -633,10 +428,7 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
                     const float hn = active ? hx : hp;   // carried when inactive
                     hreg[h][k] = hn;
                     creg[h][k] = active ? cx : cp;
-                    if constexpr (TAG)   // H before step j + 1: tag j + 2
-                        store_tagged(hbuf64 + (size_t)pj1 * plane + drow + hoff[h][k], hn, htag);
-                    else
-                        store_coherent(hnext + hoff[h][k], hn);
+                    store_coherent(hnext + hoff[h][k], hn);
                     if (a.Y) {
                         const int t = active ? (rev ? len - 1 - j : j) : j;
                         a.Y[yoff[h][k] + (size_t)t * ystep] = active ? canon_nan(hn) : 0.0f;
@@ -656,13 +448,8 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
             if (u0 + uc == a.H && Hp > a.H) {
                 const int padw = Hp - a.H;
                 const int hr = hpairs / uc;
-                for (int e = tid; e < hr * padw; e += 256) {
-                    const size_t pe = (size_t)(hrow0 + e / padw) * Hp + a.H + e % padw;
-                    if constexpr (TAG)
-                        store_tagged(hbuf64 + (size_t)pj1 * plane + drow + pe, 0.0f, htag);
-                    else
-                        store_coherent(hnext + pe, 0.0f);
-                }
+                for (int e = tid; e < hr * padw; e += 256)
+                    store_coherent(hnext + (size_t)(hrow0 + e / padw) * Hp + a.H + e % padw, 0.0f);
             }
             // published from inside the next product (there is one whenever a
             // later step exists: half 1 of this step, or half 0 of the next)

@@ -68,7 +68,6 @@ RecArgs rec_args(const rnn_plan &p, unsigned char *ws, const float *B, const flo
     r.phases = p.phases;
     r.Btp = (int32_t)p.Btp;
     r.halves = p.halves;
-    r.tagged = p.tagged;
     r.exact = p.exact;
     r.reverse_only = p.reverse_only;
     r.layout = p.layout;
@@ -319,8 +318,6 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
     ia.H = p->H;
     ia.Hp = p->Hp;
     ia.layout = p->layout;
-    ia.tagged = p->tagged;
-    ia.ring_planes = p->C + 1;
     int rc = launch_init(ia, s);
     if (rc)
         return hip_fail((hipError_t)rc, "state init");
