@@ -146,34 +146,44 @@ bool resident_ok(int nw, int nt, int nta, int phases, int kb, int mt, int pairs)
     return (mt == 2 || mt == 4) && tiles && kbs && pairs <= 2;
 }
 
-// R streamed every step (4 waves): 1, 2, 4 or 6 column tiles for one phase;
-// for two (GRU lbr=0) 1+1, 2+1 or 4+2; at most 8 pairs.
-bool streamed_ok(int nw, int nt, int nta, int phases, int pairs)
+// R streamed every step (4 waves): 1, 2, 3, 4 or 6 column tiles for one
+// phase; for two (GRU lbr=0) 1+1, 2+1 or 4+2; at most 8 pairs.  A batch tile
+// of 128 rows (mt 8) holds at most 3 column tiles (more spill registers).
+bool streamed_ok(int nw, int nt, int nta, int phases, int pairs, int mt)
 {
-    if (nw != 4)
+    if (nw != 4 || (mt == 8 && nt > 3))
         return false;
-    const bool tiles = phases == 1 ? (nt == 1 || nt == 2 || nt == 4 || nt == 6)
+    const bool tiles = phases == 1 ? (nt == 1 || nt == 2 || nt == 3 || nt == 4 || nt == 6)
                                    : ((nt == 2 && nta == 1) || (nt == 3 && nta == 2) ||
                                       (nt == 6 && nta == 4));
     return tiles && pairs <= kMaxPairs;
 }
 
-// Choose units per workgroup: at most kMaxWorkgroups workgroups, the least
-// matrix-core work per wave per step, then the fewest workgroups.
+// Choose the batch tile and the units per workgroup: at most kMaxWorkgroups
+// workgroups, the least matrix-core work per wave per step, then the larger
+// batch tile (rows are held in order of decreasing length, so a tile that
+// holds more of them keeps its workgroups busy while the shortest rows end,
+// instead of leaving a whole block of workgroups idle), then the fewest
+// workgroups.
 rnn_status choose_tiling(const rnn_attrs &a, rnn_plan &p)
 {
     if (a.batch_tile) {
-        if (a.batch_tile != 16 && a.batch_tile != 32 && a.batch_tile != 64) {
-            set_error("batch_tile must be 0, 16, 32 or 64");
+        if (a.batch_tile != 16 && a.batch_tile != 32 && a.batch_tile != 64 &&
+            a.batch_tile != 128) {
+            set_error("batch_tile must be 0, 16, 32, 64 or 128");
+            return RNN_ERR_INVALID_INPUT;
+        }
+        if (a.batch_tile == 128 && p.exact) {
+            set_error("batch_tile = 128 is a fast-mode tiling (R streamed)");
             return RNN_ERR_INVALID_INPUT;
         }
         p.BT = a.batch_tile;
     } else {
         p.BT = p.Bt <= 16 ? 16 : p.Bt <= 32 ? 32 : 64;
     }
-    p.MT = p.BT / 16;
-    p.NBB = (int32_t)std::max<int64_t>(1, (p.Bt + p.BT - 1) / p.BT);
-    p.Btp = (int64_t)p.NBB * p.BT;
+    // a tile of 128 rows is tried beside the automatic one for larger
+    // batches (fast mode, R streamed)
+    const int bt_alt = (!a.batch_tile && !p.exact && p.Bt > 64) ? 128 : 0;
     p.phases = (p.op == RNN_OP_GRU && !p.lbr) ? 2 : 1;
     if (a.waves_per_block != 0 && a.waves_per_block != 4 && a.waves_per_block != 8) {
         set_error("waves_per_block must be 0, 4 or 8");
@@ -186,6 +196,13 @@ rnn_status choose_tiling(const rnn_attrs &a, rnn_plan &p)
     };
     set_waves(a.waves_per_block ? a.waves_per_block : 4);
 
+    auto set_tile = [&](int bt) {
+        p.BT = bt;
+        p.MT = bt / 16;
+        p.NBB = (int32_t)std::max<int64_t>(1, (p.Bt + bt - 1) / bt);
+        p.Btp = (int64_t)p.NBB * bt;
+    };
+    set_tile(p.BT);
     bool cap_wg = true;   // first look for tilings whose workgroups fit at once
     auto evaluate = [&](int u, int *nta, int *ntb, bool *res, long *cost) -> bool {
         int nub = (int)((p.H + u - 1) / u);
@@ -199,16 +216,16 @@ rnn_status choose_tiling(const rnn_attrs &a, rnn_plan &p)
         int nt = *nta + *ntb;
         int pairs = (p.BT * u + nthr - 1) / nthr;
         *res = resident_ok(p.NW, nt, *nta, p.phases, p.KB, p.MT, pairs);
-        if (!*res && !streamed_ok(p.NW, nt, *nta, p.phases, pairs))
+        if (!*res && !streamed_ok(p.NW, nt, *nta, p.phases, pairs, p.MT))
             return false;
-        long lds = ((long)p.NW * p.BT * (nt * 16 + 4) + 3L * p.BT * u + p.BT + 11L * u) * 4;
+        long lds = ((long)p.NW * p.BT * (nt * 16 + 4) + 3L * p.BT * u + 2L * p.BT + 11L * u) * 4;
         if (lds > 160 * 1024)
             return false;
         *cost = (long)p.MT * nt * p.KB * 16 + (*res ? 0 : (long)p.MT * nt * p.KB * 4);
         return true;
     };
 
-    int best_u = -1, bnta = 0, bntb = 0;
+    int best_u = -1, bnta = 0, bntb = 0, bbt = p.BT;
     bool bres = false;
     long bcost = 0;
     if (a.units_per_block) {
@@ -226,23 +243,36 @@ rnn_status choose_tiling(const rnn_attrs &a, rnn_plan &p)
         best_u = u;
         bres = r;
     } else {
+        const int tiles[2] = {p.BT, bt_alt};
         for (int pass = 0; pass < 2 && best_u < 0; ++pass) {
             cap_wg = pass == 0;   // second pass: more workgroups, run one step per launch
-            for (int u = 1; u <= std::min<int64_t>(p.H, 128); ++u) {
-                int nta, ntb;
-                bool r;
-                long c;
-                if (!evaluate(u, &nta, &ntb, &r, &c))
+            for (int ti = 0; ti < 2; ++ti) {
+                if (!tiles[ti])
                     continue;
-                if (best_u < 0 || c < bcost || (c == bcost && u > best_u)) {
-                    best_u = u;
-                    bcost = c;
-                    bnta = nta;
-                    bntb = ntb;
-                    bres = r;
+                set_tile(tiles[ti]);
+                for (int u = 1; u <= std::min<int64_t>(p.H, 128); ++u) {
+                    int nta, ntb;
+                    bool r;
+                    long c;
+                    if (!evaluate(u, &nta, &ntb, &r, &c))
+                        continue;
+                    // (a 128-row tile runs the streamed kernel only)
+                    if (p.BT == 128 && r)
+                        continue;
+                    const bool better = best_u < 0 || c < bcost ||
+                                        (c == bcost && (p.BT > bbt || (p.BT == bbt && u > best_u)));
+                    if (better) {
+                        best_u = u;
+                        bcost = c;
+                        bnta = nta;
+                        bntb = ntb;
+                        bres = r;
+                        bbt = p.BT;
+                    }
                 }
             }
         }
+        set_tile(bbt);
         if (best_u < 0) {
             set_error("no recurrence tiling fits this shape");
             return RNN_ERR_UNSUPPORTED;

@@ -48,7 +48,8 @@ rec_fn RNN_CAT(rec_get_resident_a, RNN_ACT)(int nw, int mt, int nt, int kb, int 
 
 #elif RNN_FAMILY == 1 || RNN_FAMILY == 2
 // R streamed every step (4 waves), up to P_ (row, unit) pairs per thread;
-// ta as for the resident family.
+// mt 16-row tiles (a batch tile of 16 to 128 rows); ta as for the resident
+// family.
 #if RNN_FAMILY == 1
 #define P_ 2
 #define RNN_NAME rec_get_streamed2_a
@@ -64,6 +65,7 @@ rec_fn RNN_CAT(RNN_NAME, RNN_ACT)(int mt, int nt, int ta)
             switch (nt) {                                                                        \
             case 1: return rec_kernel<MT_, 1, 0, P_, 0, RNN_ACT, 4>;                             \
             case 2: return rec_kernel<MT_, 2, 0, P_, 0, RNN_ACT, 4>;                             \
+            case 3: return rec_kernel<MT_, 3, 0, P_, 0, RNN_ACT, 4>;                             \
             case 4: return rec_kernel<MT_, 4, 0, P_, 0, RNN_ACT, 4>;                             \
             case 6: return rec_kernel<MT_, 6, 0, P_, 0, RNN_ACT, 4>;                             \
             default: return nullptr;                                                             \
@@ -78,6 +80,20 @@ rec_fn RNN_CAT(RNN_NAME, RNN_ACT)(int mt, int nt, int ta)
     RNN_STR(2)
     RNN_STR(4)
 #undef RNN_STR
+    // 128-row tiles: at most 3 column tiles (wider ones spill registers)
+    if (mt == 8) {
+        if (ta == 0) {
+            switch (nt) {
+            case 1: return rec_kernel<8, 1, 0, P_, 0, RNN_ACT, 4>;
+            case 2: return rec_kernel<8, 2, 0, P_, 0, RNN_ACT, 4>;
+            case 3: return rec_kernel<8, 3, 0, P_, 0, RNN_ACT, 4>;
+            default: return nullptr;
+            }
+        }
+        if (nt == 2 && ta == 1) return rec_kernel<8, 2, 0, P_, 1, RNN_ACT, 4>;
+        if (nt == 3 && ta == 2) return rec_kernel<8, 3, 0, P_, 2, RNN_ACT, 4>;
+        return nullptr;
+    }
     return nullptr;
 }
 #undef P_

@@ -217,26 +217,27 @@ __device__ __forceinline__ void with_row_tiles(int n, F f)
 }
 
 // mt_act: row tiles that hold a row still active at this step (rows are held
-// in order of decreasing length, so they form a prefix); the MFMAs of the
-// others are skipped, their sums are never read.  Every A tile is still
-// loaded, so that the loads do not depend on mt_act.
+// in order of decreasing length, so they form a prefix).  The whole k loop --
+// A loads and MFMAs -- is specialised on that count (dispatched once per
+// step, a uniform branch), so inactive tiles cost neither loads nor matrix
+// cycles; their sums are never read.
 template <int MT, int NT, int T0, int T1, typename Mid>
 __device__ __forceinline__ void product_stream(f4 (&acc)[MT][NT], const float *asrc,
                                                const float *rfrag, int Hp, int KB, int mt_act,
                                                Mid mid)
 {
-    f4 a0[MT], b0[NT], a1[MT], b1[NT];
-    auto load = [&](f4 (&av)[MT], f4 (&bv)[NT], int kb) {
+    with_row_tiles<MT>(mt_act, [&](auto mta) {
+        constexpr int MTA = decltype(mta)::value;
+        f4 a0[MTA > 0 ? MTA : 1], b0[NT], a1[MTA > 0 ? MTA : 1], b1[NT];
+        auto load = [&](auto &av, f4 (&bv)[NT], int kb) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            av[mt] = *(const f4 *)(asrc + (size_t)mt * 16 * Hp + kb * 16);
+            for (int mt = 0; mt < MTA; ++mt)
+                av[mt] = *(const f4 *)(asrc + (size_t)mt * 16 * Hp + kb * 16);
 #pragma unroll
-        for (int nt = T0; nt < T1; ++nt)
-            bv[nt] = *(const f4 *)(rfrag + (size_t)nt * 16 * Hp + kb * 16);
-    };
-    auto mma = [&](const f4 (&av)[MT], const f4 (&bv)[NT]) {
-        with_row_tiles<MT>(mt_act, [&](auto mta) {
-            constexpr int MTA = decltype(mta)::value;
+            for (int nt = T0; nt < T1; ++nt)
+                bv[nt] = *(const f4 *)(rfrag + (size_t)nt * 16 * Hp + kb * 16);
+        };
+        auto mma = [&](const auto &av, const f4 (&bv)[NT]) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -247,25 +248,29 @@ __device__ __forceinline__ void product_stream(f4 (&acc)[MT][NT], const float *a
                                                                            acc[mt][nt], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);   // keep the independent accumulators together
             }
-        });
-    };
-    load(a0, b0, 0);
-    int kb = 0;
-    for (; kb + 2 < KB; kb += 2) {
-        load(a1, b1, kb + 1);
-        mma(a0, b0);
-        load(a0, b0, kb + 2);
-        mma(a1, b1);
-    }
-    if (KB - kb == 2) {                          // two blocks left
-        load(a1, b1, kb + 1);
-        mid();
-        mma(a0, b0);
-        mma(a1, b1);
-    } else {                                     // one block left
-        mid();
-        mma(a0, b0);
-    }
+        };
+        if constexpr (MTA == 0) {
+            mid();                                   // no active row: only the XW prefetch
+        } else {
+            load(a0, b0, 0);
+            int kb = 0;
+            for (; kb + 2 < KB; kb += 2) {
+                load(a1, b1, kb + 1);
+                mma(a0, b0);
+                load(a0, b0, kb + 2);
+                mma(a1, b1);
+            }
+            if (KB - kb == 2) {                      // two blocks left
+                load(a1, b1, kb + 1);
+                mid();
+                mma(a0, b0);
+                mma(a1, b1);
+            } else {                                 // one block left
+                mid();
+                mma(a0, b0);
+            }
+        }
+    });
 }
 
 // Gate arithmetic of one (row, unit) pair for the single-phase operators (RNN,
@@ -563,8 +568,13 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
         // resident products issue every tile: their copies per tile count
         // measured slower where all rows are active.)
         int mt_act = MT;
-        if constexpr (!RES)
-            mt_act = (__popcll(__ballot(lane < rows && lst[lane] > j)) + 15) / 16;
+        if constexpr (!RES) {
+            int na = 0;                          // active rows: a prefix of the block
+#pragma unroll
+            for (int r0 = 0; r0 < BT; r0 += 64)
+                na += __popcll(__ballot(r0 + lane < rows && lst[r0 + lane] > j));
+            mt_act = (na + 15) / 16;
+        }
         f4 acc[MT][NT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)

@@ -337,9 +337,24 @@ def test_results_do_not_depend_on_the_grid():
                               with_h0=True, with_c0=True)
     say(f"case {c.name}")
     digests = set()
-    for upb, bt in [(0, 0), (1, 16), (3, 32), (4, 64), (8, 16)]:
+    for upb, bt in [(0, 0), (1, 16), (3, 32), (4, 64), (8, 16), (0, 128), (12, 128)]:
         digests.add(_digest(run_gpu(c, units_per_block=upb, batch_tile=bt)))
     assert len(digests) == 1
+
+
+@pytest.mark.parametrize("op,attrs", [("GRU", dict(linear_before_reset=1)),
+                                      ("GRU", dict(linear_before_reset=0)), ("LSTM", {})])
+def test_batch_tile_of_128_rows_matches_oracle_and_the_64_row_tile(op, attrs):
+    # two batch blocks (128 rows and a ragged 22), lengths, R streamed
+    c = workloads.random_case(op, "reverse", 7, 150, 20, 96, seed=61, with_lens=True,
+                              with_h0=True, with_c0=(op == "LSTM"), with_p=(op == "LSTM"),
+                              scale=1.5 / 96 ** 0.5, **attrs)
+    plan = ra.plan_for_case(c, batch_tile=128)
+    say(f"case {c.name} {attrs}: {plan.describe()}")
+    assert "BT=128" in plan.describe() and "NBB=2" in plan.describe()
+    got = run_gpu(c, plan=plan)
+    compare(c, got)
+    assert _digest(got) == _digest(run_gpu(c, batch_tile=64))
 
 
 def test_repeated_runs_are_bit_identical():
