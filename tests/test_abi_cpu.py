@@ -183,7 +183,7 @@ def test_time_chunks_shrink_the_workspace_and_lift_the_scratch_limit():
 def test_workspace_and_tiling_of_the_named_workloads():
     expect = {
         "lstm_bidir_s512_b64_i1024_h1024": dict(resident="1", workgroups="256"),
-        "gru_rev_s256_b256_i2048_h2048_bf16": dict(workgroups="256", NBB="4"),
+        "gru_rev_s256_b256_i2048_h2048_bf16": dict(workgroups="256", NBB="2", BT="128", U="16"),
         "gru_fwd_s128_b32_i256_h512_lbr0": dict(phases="2"),
     }
     for name, want in expect.items():
