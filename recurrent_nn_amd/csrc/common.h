@@ -42,8 +42,8 @@ struct Layout {
     size_t sbuf = 0;    // GRU lbr=0: r (.) H_prev of step j in plane j mod C, [C][D][Btp][Hp]
     size_t cbuf = 0;    // LSTM cell state between launches [D][Bt][H]
     size_t zbuf = 0;    // GRU lbr=0 update gate between launches [D][Bt][H]
-    size_t lens = 0;    // int32 [2][Bt]: lengths by position, then the batch row at each
-                        // position (rows by decreasing length)
+    size_t lens = 0;    // int32 [3][Bt]: lengths by position, the batch row at each
+                        // position, the position of each rank (rows by decreasing length)
     size_t bar = 0;     // uint32 step flags [D*NBB][2][NUB], then int32 error word
     size_t cellb = 0;   // rnn_cell_run: summed biases expanded to [D][Wb = sum, Rb = 0]
     size_t stamps = 0;  // instrumented build only: cycle stamps [kStampSlots][kStampEvents]
@@ -82,7 +82,7 @@ struct rnn_plan {
     // tiling of the recurrence
     int32_t U = 1;            // hidden units per workgroup (last block may be ragged)
     int32_t NUB = 1;          // unit blocks per direction
-    int32_t BT = 16;          // batch rows per workgroup (16, 32 or 64)
+    int32_t BT = 16;          // batch rows per workgroup (16, 32, 64 or 128)
     int32_t NBB = 1;          // batch blocks
     int32_t MT = 1;           // 16-row MFMA tiles per workgroup (BT / 16)
     int32_t NTA = 1;          // 16-column tiles of phase 0
@@ -111,8 +111,9 @@ struct rnn_plan {
     int32_t device = -1;
 
     // timing
-    // pinned host staging of sequence_lens and their order (copied to the
-    // device asynchronously; the event guards its reuse by the next run)
+    // pinned host staging of sequence_lens, their order and sorting room,
+    // [5][Bt] (the first three copied to the device asynchronously; the
+    // event guards its reuse by the next run)
     int32_t *lens_host = nullptr;
     void *lens_event = nullptr;
     int32_t lens_pending = 0;
@@ -159,15 +160,16 @@ struct InitArgs {
 int launch_init(const InitArgs &a, void *stream);
 
 // Sequence lengths handed to the device as kernel arguments (no staging
-// buffer, no copy): the lengths by position and the batch row at each
-// position, for at most kInlineRows rows.
+// buffer, no copy): the lengths by position, the batch row at each position
+// and the position of each rank, for at most kInlineRows rows.
 constexpr int kInlineRows = 256;
 struct InlineLens {
     int32_t n;
     int32_t lens[kInlineRows];
     int32_t order[kInlineRows];
+    int32_t rank_pos[kInlineRows];
 };
-// dst[0, n) = lens, dst[n, 2n) = order
+// dst[0, n) = lens, dst[n, 2n) = order, dst[2n, 3n) = rank_pos
 int launch_lens_inline(const InlineLens &l, int32_t *dst, void *stream);
 
 struct ProjArgs {
@@ -180,7 +182,11 @@ struct ProjArgs {
     int64_t steps;          // steps held by XW (the chunk length)
     int64_t j_base;         // first step of the chunk
     const int32_t *lens;    // [Bt] lengths by position, on the device
-    const int32_t *order;   // [Bt] batch row at each position (by decreasing length), or NULL
+    const int32_t *order;   // [Bt] batch row at each position, or NULL (identity)
+    // [Bt] position of the row of rank r (ranks by decreasing length), or
+    // NULL (identity): the product walks its rows by rank, so that rows the
+    // step loop never reads fill whole tiles, and stores each at its position
+    const int32_t *rank_pos;
     int32_t reverse_only;   // direction 0 runs in reverse
     int32_t layout;         // 0: X [S][Bt][I]; 1: X [Bt][S][I]
     int32_t bf16;
@@ -200,10 +206,11 @@ struct RecArgs {
     ActSpec act[2][3];
     // buffers
     const float *Rp, *XW, *B, *P;
-    // Rows are held in order of decreasing length: position s holds batch
-    // row order[s] (identity when order is NULL), lens[s] is its length, and
-    // the H history, cell state and XW rows use positions; only the outputs
-    // Y, Y_h, Y_c use batch rows.
+    // Position s holds batch row order[s] (identity when order is NULL) and
+    // lens[s] is its length; each block of BT positions holds its rows in
+    // order of decreasing length, so that the rows still active at a step
+    // come first.  The H history, cell state and XW rows use positions; only
+    // the outputs Y, Y_h, Y_c use batch rows.
     const int32_t *lens, *order;
     float *hbuf, *sbuf, *cbuf, *zbuf;
     float *Y, *Yh, *Yc;

@@ -178,6 +178,7 @@ __global__ void lens_inline_kernel(InlineLens l, int32_t *dst)
     for (int i = threadIdx.x; i < l.n; i += blockDim.x) {
         dst[i] = l.lens[i];
         dst[l.n + i] = l.order[i];
+        dst[2 * l.n + i] = l.rank_pos[i];
     }
 }
 

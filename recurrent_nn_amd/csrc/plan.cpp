@@ -333,7 +333,7 @@ void make_layout(rnn_plan &p)
     L.sbuf = take(p.phases == 2 ? (size_t)p.C * p.D * p.Btp * p.Hp * 4 : 0);
     L.cbuf = take(p.op == RNN_OP_LSTM ? (size_t)p.D * p.Bt * p.H * 4 : 0);
     L.zbuf = take(p.phases == 2 ? (size_t)p.D * p.Bt * p.H * 4 : 0);
-    L.lens = take((size_t)std::max<int64_t>(p.Bt, 1) * 2 * 4);   // lengths by position, then order
+    L.lens = take((size_t)std::max<int64_t>(p.Bt, 1) * 3 * 4);   // lengths by position, order, positions by rank
     L.bar = take((size_t)(n_flags(p) + 1) * 4);
     L.cellb = take((size_t)p.D * 2 * GH * 4);
 #ifdef RNN_STAMPS

@@ -4,15 +4,16 @@
 // in block-column order, see pack.hip), so XW comes out in the order the
 // recurrence reads it.
 //
-// Rows.  Batch rows are held in order of decreasing length (position i
-// holds batch row order[i]), so that rows the step loop never reads cluster.
-// XW is stored by STEP: row (j - j_base, i) of direction d holds the
-// projection of the X row that step j of the row at position i reads -- time
-// j forward, len_b - 1 - j in reverse ("Choices the specification leaves
-// open": sequence_lens and reverse traversal) -- for the steps of one time
-// chunk.  Rows the step loop never reads (j >= len_b) are not computed: a
-// tile whose rows are all such is skipped.  Both directions are one launch
-// (the direction is part of the tile index).
+// Rows.  Position i holds batch row order[i]; XW is stored by STEP: row
+// (j - j_base, i) of direction d holds the projection of the X row that step
+// j of the row at position i reads -- time j forward, len_b - 1 - j in
+// reverse ("Choices the specification leaves open": sequence_lens and
+// reverse traversal) -- for the steps of one time chunk.  The product walks
+// each step's rows by rank (decreasing length; rank r sits at position
+// rank_pos[r]) and stores every row at its position, so that the rows the
+// step loop never reads (j >= len_b) come last and fill whole tiles: such
+// rows are not computed, and a tile whose rows are all such is skipped.
+// Both directions are one launch (the direction is part of the tile index).
 //
 // Tiling: 128x128 output tile per 256-thread workgroup, 4 waves of 64x64, K
 // staged through LDS in 128-byte row slices (32 fp32 or 64 bf16 values): the
@@ -114,14 +115,22 @@ __device__ __forceinline__ u4 pack8(f4 a, f4 b)
     return v;
 }
 
-// X row read by logical row m = (j - j_base) * Bt + i of direction d, i.e.
-// step j of the batch row at position i; -1 when the step loop never reads it
-// (j >= len) or m is past the chunk.
+// Logical row m = (j - j_base) * Bt + r of the product is step j of the row
+// of rank r.  Its XW row (step j - j_base, the row's position):
+__device__ __forceinline__ int64_t proj_outrow(const ProjArgs &a, int64_t m)
+{
+    const uint32_t jl = (uint32_t)m / (uint32_t)a.Bt, r = (uint32_t)m - jl * (uint32_t)a.Bt;
+    return (int64_t)jl * a.Bt + (a.rank_pos ? a.rank_pos[r] : r);
+}
+
+// The X row that logical row m of direction d reads; -1 when the step loop
+// never reads it (j >= len) or m is past the chunk.
 __device__ __forceinline__ int64_t proj_xrow(const ProjArgs &a, int64_t d, int64_t m)
 {
     if (m >= a.steps * a.Bt)
         return -1;
-    const uint32_t jl = (uint32_t)m / (uint32_t)a.Bt, i = (uint32_t)m - jl * (uint32_t)a.Bt;
+    const uint32_t jl = (uint32_t)m / (uint32_t)a.Bt, r = (uint32_t)m - jl * (uint32_t)a.Bt;
+    const int64_t i = a.rank_pos ? a.rank_pos[r] : r;   // position of rank r
     const int64_t b = a.order ? a.order[i] : i;          // position i holds batch row b
     const int64_t j = a.j_base + jl, len = a.lens[i];
     if (j >= len)
@@ -338,8 +347,8 @@ __global__ void __launch_bounds__(256, 3) proj_gemm_kernel(ProjArgs a)
         }
     }
 
-    // store: lane holds rows 4*lq + r, column lr of each 16x16 tile; row
-    // m = (j - j_base) * Bt + i is XW's row for step j, position i
+    // store: lane holds rows 4*lq + r, column lr of each 16x16 tile;
+    // logical row m goes to XW's row for its step and position
     float *XWd = a.XW + (size_t)d * Md * a.GH;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -348,7 +357,7 @@ __global__ void __launch_bounds__(256, 3) proj_gemm_kernel(ProjArgs a)
             const int64_t m = m0 + wm * 64 + i * 16 + lq * 4 + r;
             if (m >= Md)
                 continue;
-            const size_t ro = (size_t)m * a.GH;
+            const size_t ro = (size_t)proj_outrow(a, m) * a.GH;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t n = n0 + wn * 64 + j * 16 + lr;
@@ -479,7 +488,7 @@ __global__ void __launch_bounds__(256) proj_exact_kernel(ProjArgs a)
         const int64_t m = m0 + 4 * ty + i;
         if (m >= Md)
             continue;
-        const size_t ro = (size_t)m * a.GH;     // step j - j_base, position i
+        const size_t ro = (size_t)proj_outrow(a, m) * a.GH;   // step, position
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t n = n0 + 4 * tx + j;

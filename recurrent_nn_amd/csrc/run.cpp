@@ -138,16 +138,40 @@ rnn_status ensure_events(rnn_plan *p)
     return RNN_OK;
 }
 
-// The batch rows in order of decreasing length (ties by row): order[i] is
-// the row held at position i and byPos[i] its length.  The kernels hold rows
-// in this order, so that the rows still active at a step come first.
-void order_rows(const int32_t *lens, int64_t Bt, int32_t *byPos, int32_t *order)
+// The batch rows by decreasing length (ties by lower row) -- their ranks --
+// dealt over the batch blocks of BT positions (the last block may hold
+// fewer) in proportion to each block's capacity: slot k of a block of cap
+// rows falls at the fraction (k + 1/2) / cap of the deal, slots are taken in
+// that order (lower block first on ties) and rank r fills the r-th slot.
+// With equal blocks this is round robin.  Every block then holds a run of
+// decreasing lengths (its active rows come first) and a like share of every
+// length, which matters because the step loop waits for its slowest block
+// at every step.  order[i] is the batch row at position i, byPos[i] its
+// length, rank_pos[r] the position of the row of rank r; tmp holds 2 Bt
+// values.  Nothing is allocated.
+void order_rows(const int32_t *lens, int64_t Bt, int64_t BT, int32_t *byPos, int32_t *order,
+                int32_t *rank_pos, int32_t *tmp)
 {
+    int32_t *rank = tmp, *slot = tmp + Bt;
     for (int64_t b = 0; b < Bt; ++b)
-        order[b] = (int32_t)b;
-    std::stable_sort(order, order + Bt, [lens](int32_t x, int32_t y) { return lens[x] > lens[y]; });
+        rank[b] = (int32_t)b;
+    std::sort(rank, rank + Bt, [lens](int32_t x, int32_t y) {
+        return lens[x] != lens[y] ? lens[x] > lens[y] : x < y;
+    });
     for (int64_t i = 0; i < Bt; ++i)
-        byPos[i] = lens[order[i]];
+        slot[i] = (int32_t)i;          // position i = block i / BT, slot i % BT
+    auto cap = [Bt, BT](int64_t blk) { return std::min<int64_t>(BT, Bt - blk * BT); };
+    std::sort(slot, slot + Bt, [&](int32_t x, int32_t y) {
+        const int64_t bx = x / BT, by = y / BT;
+        const int64_t fx = (2 * (x - bx * BT) + 1) * cap(by), fy = (2 * (y - by * BT) + 1) * cap(bx);
+        return fx != fy ? fx < fy : bx < by;
+    });
+    for (int64_t r = 0; r < Bt; ++r) {
+        const int32_t pos = slot[r];
+        order[pos] = rank[r];
+        byPos[pos] = lens[rank[r]];
+        rank_pos[r] = pos;
+    }
 }
 
 
@@ -264,7 +288,8 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
         // the lengths by position and the row order as kernel arguments
         InlineLens il;
         il.n = (int32_t)p->Bt;
-        order_rows(sequence_lens, p->Bt, il.lens, il.order);
+        int32_t tmp[2 * kInlineRows];
+        order_rows(sequence_lens, p->Bt, p->BT, il.lens, il.order, il.rank_pos, tmp);
         int rc = launch_lens_inline(il, lens_dev, s);
         if (rc)
             return hip_fail((hipError_t)rc, "sequence_lens (kernel arguments)");
@@ -273,7 +298,7 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
         // the lengths by position and the row order, staged in pinned memory
         // owned by the plan and copied on the stream
         if (!p->lens_host) {
-            e = hipHostMalloc((void **)&p->lens_host, (size_t)p->Bt * 3 * sizeof(int32_t),
+            e = hipHostMalloc((void **)&p->lens_host, (size_t)p->Bt * 5 * sizeof(int32_t),
                               hipHostMallocDefault);
             if (e != hipSuccess)
                 return hip_fail(e, "hipHostMalloc (sequence_lens staging)");
@@ -289,9 +314,11 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
                 return hip_fail(e, "hipEventSynchronize (sequence_lens staging)");
             p->lens_pending = 0;
         }
-        int32_t *hs = p->lens_host, *ho = hs + p->Bt;   // by position, then the order
-        order_rows(sequence_lens, p->Bt, hs, ho);
-        e = hipMemcpyAsync(lens_dev, hs, (size_t)p->Bt * 2 * sizeof(int32_t),
+        // lengths by position, the order, the positions by rank, then 2 Bt
+        // values of sorting room (not copied)
+        int32_t *hs = p->lens_host;
+        order_rows(sequence_lens, p->Bt, p->BT, hs, hs + p->Bt, hs + 2 * p->Bt, hs + 3 * p->Bt);
+        e = hipMemcpyAsync(lens_dev, hs, (size_t)p->Bt * 3 * sizeof(int32_t),
                            hipMemcpyHostToDevice, s);
         if (e != hipSuccess)
             return hip_fail(e, "sequence_lens copy");
@@ -346,6 +373,7 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
         pr.j_base = j0;
         pr.lens = lens_dev;
         pr.order = order_dev;
+        pr.rank_pos = order_dev ? order_dev + p->Bt : nullptr;
         pr.reverse_only = p->reverse_only;
         pr.layout = p->layout;
         pr.bf16 = p->proj_bf16;
