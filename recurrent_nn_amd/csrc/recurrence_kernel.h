@@ -659,9 +659,83 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
             }
         };
 
-        // (up to 8 pairs: one pair per iteration, not unrolled, since the
-        // unrolled form ran out of registers; the pair's XW values are moved
-        // down the array instead of indexed at run time)
+        // One-phase gates of N pairs (N = 1 or 2) of this thread: every LDS
+        // value they read (the waves' partial sums of their gate columns, the
+        // constants of their units, their states and rows) is loaded first,
+        // the gates are computed for every pair and kept only while its row is
+        // active, and the stores come last -- no branch separates the loads
+        // from their use, and the pairs' chains interleave.
+        auto gates_n = [&](auto NC, const int *pis, const float (*xv)[4], auto F, auto Gf,
+                           auto Hf) {
+            constexpr int N = decltype(NC)::value;
+            int rl[N], u[N], len[N];
+            float hp[N], cp[N], part[N][4][kWaves], cv[N][11];
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                rl[n] = pis[n] / uc;
+                u[n] = pis[n] - rl[n] * uc;
+                len[n] = lst[rl[n]];
+                hp[n] = hst[pis[n]];
+                cp[n] = cst[pis[n]];
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int w2 = 0; w2 < kWaves; ++w2)
+                        part[n][g][w2] = g < G ? red[(w2 * BT + rl[n]) * LDR + g * uc + u[n]] : 0.0f;
+#pragma unroll
+                for (int e = 0; e < 11; ++e) {
+                    const bool need = op == RNN_OP_RNN   ? (e == 0 || e == 4)
+                                      : op == RNN_OP_GRU ? (e < 8 && e % 4 < 3)
+                                                         : (e < 8 || Pd != nullptr);
+                    cv[n][e] = need ? cst_u[e * a.U + u[n]] : 0.0f;
+                }
+            }
+            float hn[N], cn[N];
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                float cx = cp[n];
+                const float hx = gates_one_phase(
+                    op, xv[n],
+                    [&](int g) {
+                        float v = part[n][g][0];
+#pragma unroll
+                        for (int w2 = 1; w2 < kWaves; ++w2)
+                            v = v + part[n][g][w2];               // fixed wave order
+                        return v;
+                    },
+                    [&](int e) { return cv[n][e]; }, Pd != nullptr, a.clip_on, a.clip,
+                    a.input_forget != 0, hp[n], cx, F, Gf, Hf);
+                const bool active = j < len[n];
+                hn[n] = active ? hx : hp[n];                      // carried when inactive
+                cn[n] = active ? cx : cp[n];
+            }
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                store_coherent(hnext + (size_t)rl[n] * Hp + u0 + u[n], hn[n]);
+                hst[pis[n]] = hn[n];
+                cst[pis[n]] = cn[n];
+            }
+            if (a.Y) {
+#pragma unroll
+                for (int n = 0; n < N; ++n) {
+                    const bool active = j < len[n];
+                    const int b = ost[rl[n]];                     // batch row (outputs)
+                    const int t = active ? (rev ? len[n] - 1 - j : j) : j;
+                    const size_t yo = a.layout == 0
+                                          ? (((size_t)t * a.D + d) * a.Bt + b) * a.H + u0 + u[n]
+                                          : (((size_t)b * a.S + t) * a.D + d) * a.H + u0 + u[n];
+                    a.Y[yo] = active ? canon_nan(hn[n]) : 0.0f;
+                }
+            }
+        };
+
+        // Pairs tid + kThreads i.  Up to 2 pairs: one at a time, unrolled.  Up
+        // to 8 pairs, one phase: two at a time where every thread has both (a
+        // uniform test), in a loop that is not unrolled -- unrolled, the LDS
+        // addresses of every pair are hoisted out of the step loop and spill
+        // -- with the pairs' XW values moved down the array instead of
+        // indexed at run time.  Up to 8 pairs, two phases (GRU,
+        // linear_before_reset 0): one at a time, likewise.
         auto run_pairs = [&](auto F, auto Gf, auto Hf) {
             if constexpr (P <= 2) {
 #pragma unroll
@@ -670,19 +744,42 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
                     if (pi < npairs)
                         do_pair(pi, xw[i], F, Gf, Hf);
                 }
-                return;
-            }
+            } else if constexpr (PH == 1) {
+                static_assert(P % 2 == 0, "pairs are taken two at a time");
 #pragma unroll 1
-            for (int i = 0; i < P; ++i) {
-                const int pi = tid + kThreads * i;
-                if (pi >= npairs)
-                    break;
-                do_pair(pi, xw[0], F, Gf, Hf);
+                for (int i = 0; i < P; i += 2) {
+                    const int pi0 = tid + kThreads * i;
+                    if (npairs >= kThreads * (i + 2)) {
+                        const int pis[2] = {pi0, pi0 + kThreads};
+                        gates_n(std::integral_constant<int, 2>{}, pis, xw, F, Gf, Hf);
+                    } else {
+                        if (pi0 < npairs)
+                            gates_n(std::integral_constant<int, 1>{}, &pi0, xw, F, Gf, Hf);
+                        const int pi1 = pi0 + kThreads;
+                        if (pi1 < npairs)
+                            gates_n(std::integral_constant<int, 1>{}, &pi1, xw + 1, F, Gf, Hf);
+                    }
+                    if (npairs <= kThreads * (i + 2))
+                        break;
 #pragma unroll
-                for (int k = 0; k + 1 < P; ++k)
+                    for (int k = 0; k + 2 < P; ++k)
 #pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        xw[k][g] = xw[k + 1][g];
+                        for (int g = 0; g < 4; ++g)
+                            xw[k][g] = xw[k + 2][g];
+                }
+            } else {
+#pragma unroll 1
+                for (int i = 0; i < P; ++i) {
+                    const int pi = tid + kThreads * i;
+                    if (pi >= npairs)
+                        break;
+                    do_pair(pi, xw[0], F, Gf, Hf);
+#pragma unroll
+                    for (int k = 0; k + 1 < P; ++k)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g)
+                            xw[k][g] = xw[k + 1][g];
+                }
             }
         };
         // ACT (compile time): 1 LSTM Sigmoid/Tanh/Tanh, 2 GRU HardSigmoid/Tanh,
