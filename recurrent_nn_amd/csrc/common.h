@@ -42,6 +42,7 @@ struct Layout {
     size_t sbuf = 0;    // GRU lbr=0: r (.) H_prev of step j in plane j mod C, [C][D][Btp][Hp]
     size_t cbuf = 0;    // LSTM cell state between launches [D][Bt][H]
     size_t zbuf = 0;    // GRU lbr=0 update gate between launches [D][Bt][H]
+    size_t rowmap = 0;  // int32 [C * Bt]: the projection's rows of a time chunk
     size_t lens = 0;    // int32 [3][Bt]: lengths by position, the batch row at each
                         // position, the position of each rank (rows by decreasing length)
     size_t bar = 0;     // uint32 step flags [D*NBB][2][NUB], then int32 error word
@@ -74,6 +75,7 @@ struct rnn_plan {
     int32_t kernel_path = 0;
     uint32_t spin_limit = 0;  // polls before a step barrier gives up
     int32_t withhold_flags = 0;   // test fault injection: step flags are never stored
+    int32_t proj_rows = 0;    // projection rows with sequence_lens: 0 auto, 1 list, 2 tiles
     int32_t stamp_wg = 0;     // instrumented build: the workgroup whose steps are stamped
     int64_t S = 0, Bt = 0, I = 0, H = 0;
     int64_t C = 0;            // steps per chunk (time_chunk; S when not chunked)
@@ -187,12 +189,21 @@ struct ProjArgs {
     // NULL (identity): the product walks its rows by rank, so that rows the
     // step loop never reads fill whole tiles, and stores each at its position
     const int32_t *rank_pos;
+    // The rows computed.  With rowmap (sequence_lens given): m_rows rows, row
+    // m' being dense row rowmap[m'] = (j - j_base) * Bt + r, the rows the step
+    // loop reads, step by step (built by launch_proj_rows).  Without it:
+    // m_rows = steps * Bt dense rows.
+    const int32_t *rowmap;
+    int64_t m_rows;
     int32_t reverse_only;   // direction 0 runs in reverse
     int32_t layout;         // 0: X [S][Bt][I]; 1: X [Bt][S][I]
     int32_t bf16;
     int32_t exact;          // exact mode: one accumulator per output, k in order, VALU
 };
 int launch_projection(const ProjArgs &a, void *stream);
+// rowmap[0, m_rows) of the chunk, from the lengths by position and the
+// positions by rank (one workgroup)
+int launch_proj_rows(const ProjArgs &a, int32_t *rowmap, void *stream);
 
 struct RecArgs {
     // sizes

@@ -333,6 +333,7 @@ void make_layout(rnn_plan &p)
     L.sbuf = take(p.phases == 2 ? (size_t)p.C * p.D * p.Btp * p.Hp * 4 : 0);
     L.cbuf = take(p.op == RNN_OP_LSTM ? (size_t)p.D * p.Bt * p.H * 4 : 0);
     L.zbuf = take(p.phases == 2 ? (size_t)p.D * p.Bt * p.H * 4 : 0);
+    L.rowmap = take((size_t)p.C * std::max<int64_t>(p.Bt, 1) * 4);
     L.lens = take((size_t)std::max<int64_t>(p.Bt, 1) * 3 * 4);   // lengths by position, order, positions by rank
     L.bar = take((size_t)(n_flags(p) + 1) * 4);
     L.cellb = take((size_t)p.D * 2 * GH * 4);
@@ -430,6 +431,13 @@ extern "C" rnn_status rnn_plan_create(const rnn_attrs *attrs, const rnn_dims *di
     {
         const char *e = std::getenv("RNN_AMD_TEST_WITHHOLD_FLAGS");
         p->withhold_flags = (e && *e && *e != '0') ? 1 : 0;
+    }
+    // Which rows the projection computes with sequence_lens (test switch):
+    // "list" always the list of rows read, "tiles" always whole tiles (those
+    // with no row read skipped); unset, the list when the product is large.
+    {
+        const char *e = std::getenv("RNN_AMD_TEST_PROJ_ROWS");
+        p->proj_rows = !e ? 0 : std::strcmp(e, "list") == 0 ? 1 : std::strcmp(e, "tiles") == 0 ? 2 : 0;
     }
 #ifdef RNN_STAMPS
     {

@@ -8,12 +8,14 @@
 // (j - j_base, i) of direction d holds the projection of the X row that step
 // j of the row at position i reads -- time j forward, len_b - 1 - j in
 // reverse ("Choices the specification leaves open": sequence_lens and
-// reverse traversal) -- for the steps of one time chunk.  The product walks
-// each step's rows by rank (decreasing length; rank r sits at position
-// rank_pos[r]) and stores every row at its position, so that the rows the
-// step loop never reads (j >= len_b) come last and fill whole tiles: such
-// rows are not computed, and a tile whose rows are all such is skipped.
-// Both directions are one launch (the direction is part of the tile index).
+// reverse traversal) -- for the steps of one time chunk.  Dense row
+// m = (j - j_base) * Bt + r is step j of the row of rank r (decreasing
+// length; rank r sits at position rank_pos[r]), stored at the row's
+// position.  With sequence_lens the product computes only the rows the step
+// loop reads (j < len_b): at step j those are the ranks below the number of
+// rows still active, and rowmap lists them step by step (built on the device
+// per chunk), so the rows computed are one dense list with no holes.  Both
+// directions are one launch (the direction is part of the tile index).
 //
 // Tiling: 128x128 output tile per 256-thread workgroup, 4 waves of 64x64, K
 // staged through LDS in 128-byte row slices (32 fp32 or 64 bf16 values): the
@@ -139,17 +141,77 @@ __device__ __forceinline__ int64_t proj_xrow(const ProjArgs &a, int64_t d, int64
     return a.layout == 0 ? t * a.Bt + b : b * a.S + t;
 }
 
-// bf16 projection: the chunk's X rows in step order, rounded to bfloat16
-// (nearest even) once, zeros for rows never read; the product then reads
-// bf16 rows directly instead of converting in every N tile.
+// Dense row of computed row mc.
+__device__ __forceinline__ int64_t proj_dense(const ProjArgs &a, int64_t mc)
+{
+    return a.rowmap ? (int64_t)a.rowmap[mc] : mc;
+}
+
+// The rows the step loop reads in the chunk, step by step: step jl reads the
+// ranks r < na(j) (na(j) = rows with length > j; lengths by rank do not
+// increase), listed as jl * Bt + r.  One workgroup: 1024 steps at a time, the
+// counts by binary search, their exclusive scan, then the rows of each step
+// written by all threads.
+__global__ void __launch_bounds__(1024) proj_rows_kernel(ProjArgs a, int32_t *rowmap)
+{
+    __shared__ int32_t cnt[1024], off[1024];
+    const int tid = threadIdx.x;
+    int64_t base = 0;
+    for (int64_t s0 = 0; s0 < a.steps; s0 += 1024) {
+        const int64_t jl = s0 + tid;
+        int32_t na = 0;
+        if (jl < a.steps) {
+            const int64_t j = a.j_base + jl;
+            int lo = 0, hi = (int)a.Bt;                 // first rank whose length <= j
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (a.lens[a.rank_pos[mid]] > j)
+                    lo = mid + 1;
+                else
+                    hi = mid;
+            }
+            na = lo;
+        }
+        cnt[tid] = na;
+        off[tid] = na;
+        __syncthreads();
+        for (int o = 1; o < 1024; o <<= 1) {            // inclusive scan of the counts
+            const int32_t v = tid >= o ? off[tid - o] : 0;
+            __syncthreads();
+            off[tid] += v;
+            __syncthreads();
+        }
+        const int nsteps = (int)(a.steps - s0 < 1024 ? a.steps - s0 : 1024);
+        for (int k = 0; k < nsteps; ++k) {
+            const int64_t o = base + off[k] - cnt[k];
+            const int32_t first = (int32_t)((s0 + k) * a.Bt);
+            for (int r = tid; r < cnt[k]; r += 1024)
+                rowmap[o + r] = first + r;
+        }
+        base += off[nsteps - 1];
+        __syncthreads();                                 // before cnt and off are reused
+    }
+}
+
+int launch_proj_rows(const ProjArgs &a, int32_t *rowmap, void *stream)
+{
+    if (a.steps <= 0 || a.Bt <= 0)
+        return 0;
+    hipLaunchKernelGGL(proj_rows_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, a, rowmap);
+    return (int)hipGetLastError();
+}
+
+// bf16 projection: the chunk's computed X rows in order, rounded to
+// bfloat16 (nearest even) once, zeros for rows never read; the product then
+// reads bf16 rows directly instead of converting in every N tile.
 __global__ void gather_bf16_kernel(ProjArgs a)
 {
-    const int64_t Md = a.steps * a.Bt;
+    const int64_t Mc = a.m_rows;
     const float *X = (const float *)a.X;
     const bool vec = a.K % 8 == 0;
-    for (int64_t row = blockIdx.x; row < a.D * Md; row += gridDim.x) {
-        const int64_t d = row / Md, m = row - d * Md;
-        const int64_t xr = proj_xrow(a, d, m);
+    for (int64_t row = blockIdx.x; row < a.D * Mc; row += gridDim.x) {
+        const int64_t d = row / Mc, m = row - d * Mc;
+        const int64_t xr = proj_xrow(a, d, proj_dense(a, m));
         uint16_t *dst = a.Xb + row * a.K;
         const float *src = xr >= 0 ? X + xr * a.K : nullptr;
         if (vec) {
@@ -195,8 +257,9 @@ __global__ void __launch_bounds__(256, 3) proj_gemm_kernel(ProjArgs a)
     const int lr = lane & 15, lq = lane >> 4;
     const int wm = w >> 1, wn = w & 1;
 
-    const int64_t Md = a.steps * a.Bt;                 // rows per direction
-    const int64_t tiles_m = (Md + BM - 1) / BM, tiles_n = (a.GH + BN - 1) / BN;
+    const int64_t Md = a.steps * a.Bt;                 // XW rows per direction
+    const int64_t Mc = a.m_rows;                       // rows computed per direction
+    const int64_t tiles_m = (Mc + BM - 1) / BM, tiles_n = (a.GH + BN - 1) / BN;
     int64_t tmg, tn;
     tile_of(blockIdx.x, gridDim.x, a.D * tiles_m, tiles_n, &tmg, &tn);
     const int64_t d = tmg / tiles_m, tm = tmg - d * tiles_m;
@@ -213,7 +276,7 @@ __global__ void __launch_bounds__(256, 3) proj_gemm_kernel(ProjArgs a)
     // partial last stage, and operands of 2 GiB or more, take the checked
     // loads.
     constexpr int ESZ = BF16 ? 2 : 4;
-    const int64_t a_bytes = BF16 ? a.D * Md * a.K * 2 : a.S * a.Bt * a.K * 4;
+    const int64_t a_bytes = BF16 ? a.D * Mc * a.K * 2 : a.S * a.Bt * a.K * 4;
     const int64_t b_bytes = a.GH * a.K * ESZ;
     const bool fast = (BF16 ? a.K % 8 == 0 : a.K % 4 == 0) && a_bytes < (int64_t)kOffNone &&
                       b_bytes < (int64_t)kOffNone;
@@ -225,7 +288,8 @@ __global__ void __launch_bounds__(256, 3) proj_gemm_kernel(ProjArgs a)
     int any = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        xr[i] = proj_xrow(a, d, m0 + srow + 32 * i);
+        const int64_t m = m0 + srow + 32 * i;
+        xr[i] = m < Mc ? proj_xrow(a, d, proj_dense(a, m)) : -1;
         any |= xr[i] >= 0;
     }
     if (!__syncthreads_or(any))
@@ -237,7 +301,7 @@ __global__ void __launch_bounds__(256, 3) proj_gemm_kernel(ProjArgs a)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t row = srow + 32 * i;
-        const int64_t ar = BF16 ? (m0 + row < Md ? d * Md + m0 + row : -1) : xr[i];
+        const int64_t ar = BF16 ? (m0 + row < Mc ? d * Mc + m0 + row : -1) : xr[i];
         aoff[i] = ar >= 0 ? (uint32_t)(ar * a.K * ESZ) + sch * 16 : kOffNone;
         boff[i] = n0 + row < a.GH ? (uint32_t)((n0 + row) * a.K * ESZ) + sch * 16 : kOffNone;
     }
@@ -257,7 +321,7 @@ __global__ void __launch_bounds__(256, 3) proj_gemm_kernel(ProjArgs a)
             const int64_t row = srow + 32 * i;
             if constexpr (BF16) {
                 const int64_t k = kbase + sch * 8;
-                ra[i] = load8h(a.Xb + (size_t)d * Md * a.K, m0 + row, k, Md, a.K, b_vec);
+                ra[i] = load8h(a.Xb + (size_t)d * Mc * a.K, m0 + row, k, Mc, a.K, b_vec);
                 rb[i] = load8h((const uint16_t *)Wd, n0 + row, k, a.GH, a.K, b_vec);
             } else {
                 const int64_t k = kbase + sch * 4;
@@ -355,9 +419,9 @@ __global__ void __launch_bounds__(256, 3) proj_gemm_kernel(ProjArgs a)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t m = m0 + wm * 64 + i * 16 + lq * 4 + r;
-            if (m >= Md)
+            if (m >= Mc)
                 continue;
-            const size_t ro = (size_t)proj_outrow(a, m) * a.GH;
+            const size_t ro = (size_t)proj_outrow(a, proj_dense(a, m)) * a.GH;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t n = n0 + wn * 64 + j * 16 + lr;
@@ -385,20 +449,21 @@ __global__ void __launch_bounds__(256) proj_exact_kernel(ProjArgs a)
     __shared__ __attribute__((aligned(16))) float As[KC][LDT], Bs[KC][LDT];
     __shared__ int64_t xrow_s[TM];
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-    const int64_t Md = a.steps * a.Bt;
-    const int64_t tiles_m = (Md + TM - 1) / TM, tiles_n = (a.GH + TN - 1) / TN;
+    const int64_t Md = a.steps * a.Bt;                 // XW rows per direction
+    const int64_t Mc = a.m_rows;                       // rows computed per direction
+    const int64_t tiles_m = (Mc + TM - 1) / TM, tiles_n = (a.GH + TN - 1) / TN;
     const int64_t tmg = blockIdx.x / tiles_n, tn = blockIdx.x - tmg * tiles_n;
     const int64_t d = tmg / tiles_m, tm = tmg - d * tiles_m;
     const int64_t m0 = tm * TM, n0 = tn * TN;
     int any = 0;
     if (tid < TM) {
-        xrow_s[tid] = proj_xrow(a, d, m0 + tid);
+        xrow_s[tid] = m0 + tid < Mc ? proj_xrow(a, d, proj_dense(a, m0 + tid)) : -1;
         any = xrow_s[tid] >= 0;
     }
     if (!__syncthreads_or(any))
         return;                                      // no row of this tile is ever read
     const float *X = (const float *)a.X;
-    const uint16_t *Xb = BF16 ? a.Xb + (size_t)d * Md * a.K : nullptr;
+    const uint16_t *Xb = BF16 ? a.Xb + (size_t)d * Mc * a.K : nullptr;
     const char *Wd = (const char *)a.Wp + (size_t)d * a.GH * a.K * (BF16 ? 2 : 4);
     auto bf = [](uint32_t h) { return __uint_as_float(h << 16); };
 
@@ -406,7 +471,7 @@ __global__ void __launch_bounds__(256) proj_exact_kernel(ProjArgs a)
     const int sr = tid >> 3, sk = (tid & 7) * 4;
     auto row_a = [&](int r) -> int64_t {        // source row of A, or -1
         if (BF16)
-            return m0 + r < Md ? m0 + r : -1;
+            return m0 + r < Mc ? m0 + r : -1;
         return xrow_s[r];
     };
     auto row_b = [&](int r) -> int64_t { return n0 + r < a.GH ? n0 + r : -1; };
@@ -486,9 +551,9 @@ __global__ void __launch_bounds__(256) proj_exact_kernel(ProjArgs a)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t m = m0 + 4 * ty + i;
-        if (m >= Md)
+        if (m >= Mc)
             continue;
-        const size_t ro = (size_t)proj_outrow(a, m) * a.GH;   // step, position
+        const size_t ro = (size_t)proj_outrow(a, proj_dense(a, m)) * a.GH;   // step, position
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t n = n0 + 4 * tx + j;
@@ -500,17 +565,17 @@ __global__ void __launch_bounds__(256) proj_exact_kernel(ProjArgs a)
 
 int launch_projection(const ProjArgs &a, void *stream)
 {
-    if (a.steps <= 0 || a.Bt <= 0 || a.GH <= 0)
+    if (a.steps <= 0 || a.Bt <= 0 || a.GH <= 0 || a.m_rows <= 0)
         return 0;
     if (a.exact) {
         if (a.bf16) {
-            int64_t blocks = a.D * a.steps * a.Bt;
+            int64_t blocks = a.D * a.m_rows;
             if (blocks > 65536)
                 blocks = 65536;
             hipLaunchKernelGGL(gather_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0,
                                (hipStream_t)stream, a);
         }
-        const int64_t et = a.D * ((a.steps * a.Bt + 63) / 64) * ((a.GH + 63) / 64);
+        const int64_t et = a.D * ((a.m_rows + 63) / 64) * ((a.GH + 63) / 64);
         if (a.bf16)
             hipLaunchKernelGGL(proj_exact_kernel<true>, dim3((unsigned)et), dim3(256), 0,
                                (hipStream_t)stream, a);
@@ -519,14 +584,14 @@ int launch_projection(const ProjArgs &a, void *stream)
                                (hipStream_t)stream, a);
         return (int)hipGetLastError();
     }
-    const int64_t tiles = a.D * ((a.steps * a.Bt + BM - 1) / BM) * ((a.GH + BN - 1) / BN);
+    const int64_t tiles = a.D * ((a.m_rows + BM - 1) / BM) * ((a.GH + BN - 1) / BN);
     const size_t shmem = 2 * TILEB;               // one buffer of A and B
     const void *fn = a.bf16 ? (const void *)proj_gemm_kernel<true> : (const void *)proj_gemm_kernel<false>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess)
         return (int)e;
     if (a.bf16) {
-        int64_t blocks = a.D * a.steps * a.Bt;
+        int64_t blocks = a.D * a.m_rows;
         if (blocks > 65536)
             blocks = 65536;
         hipLaunchKernelGGL(gather_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0,

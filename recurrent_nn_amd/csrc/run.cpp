@@ -374,6 +374,24 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
         pr.lens = lens_dev;
         pr.order = order_dev;
         pr.rank_pos = order_dev ? order_dev + p->Bt : nullptr;
+        // With sequence_lens and a product of many tiles, only the rows the
+        // step loop reads in this chunk, listed on the device (for a small
+        // product the extra launch costs more than the rows it saves, and
+        // whole tiles with no row read are skipped anyway).
+        pr.m_rows = p->C * p->Bt;
+        const int64_t dense_tiles = p->D * ((p->C * p->Bt + 127) / 128) * ((pr.GH + 127) / 128);
+        const bool row_list = sequence_lens && (p->proj_rows == 1 ||
+                                                (p->proj_rows == 0 && dense_tiles >= 2048));
+        if (row_list) {
+            pr.m_rows = 0;
+            for (int64_t b = 0; b < p->Bt; ++b)
+                pr.m_rows += std::min<int64_t>(p->C, std::max<int64_t>(0, sequence_lens[b] - j0));
+            int32_t *rowmap = (int32_t *)(ws + p->ws.rowmap);
+            pr.rowmap = rowmap;
+            rc = launch_proj_rows(pr, rowmap, s);
+            if (rc)
+                return hip_fail((hipError_t)rc, "projection rows");
+        }
         pr.reverse_only = p->reverse_only;
         pr.layout = p->layout;
         pr.bf16 = p->proj_bf16;

@@ -535,3 +535,29 @@ def test_many_step_handover_matches_oracle(op, attrs):
         t = int(np.argwhere(bad)[0][0])
         raise AssertionError(f"first step differing: {t} (max abs there {err[t].max():.3e})")
     compare(c, gpu, ref, strict=True)
+
+
+@pytest.mark.parametrize("proj_bf16,exact", [(False, False), (True, False), (False, True),
+                                             (True, True)])
+def test_projection_row_list_and_whole_tiles_agree_bitwise(proj_bf16, exact, monkeypatch):
+    # With sequence_lens the projection computes either the list of rows the
+    # step loop reads (built on the device per time chunk) or whole tiles;
+    # both give the same bits.  Lengths from 0 to seq, two directions, three
+    # time chunks (so the list starts at steps j_base > 0).
+    c = workloads.random_case("GRU", "bidirectional", 13, 70, 40, 48, seed=71, with_lens=True,
+                              with_h0=True, linear_before_reset=1, proj_bf16=proj_bf16,
+                              scale=1.5 / 48 ** 0.5)
+    say(f"case {c.name} bf16={proj_bf16} exact={exact}")
+    outs = []
+    for mode in ("list", "tiles"):
+        monkeypatch.setenv("RNN_AMD_TEST_PROJ_ROWS", mode)
+        outs.append(run_gpu(c, exact=exact, time_chunk=5))
+    monkeypatch.delenv("RNN_AMD_TEST_PROJ_ROWS")
+    assert _digest(outs[0]) == _digest(outs[1])
+    ref = oracle_outputs(c)
+    if exact:
+        for what, g, r in zip(("Y", "Y_h"), outs[0], ref):
+            assert np.array_equal(u32(g), u32(r)), f"{what}: not bit-exact"
+        check_masks(c, *outs[0])
+    else:
+        compare(c, outs[0], ref)
