@@ -561,3 +561,25 @@ def test_projection_row_list_and_whole_tiles_agree_bitwise(proj_bf16, exact, mon
         check_masks(c, *outs[0])
     else:
         compare(c, outs[0], ref)
+
+
+def test_long_two_half_run_matches_oracle():
+    # the two-half kernel with the LSTM benchmark workload's tile shape (64
+    # rows in two halves, R resident, 16 k blocks per wave; one column tile)
+    # over 2048 steps, i.e. 4096 hand-overs per workgroup; every element is
+    # compared, and the first step that differs is named
+    c = workloads.random_case("LSTM", "forward", 2048, 64, 64, 1024, seed=83, with_h0=True,
+                              with_c0=True, scale=1.0 / 32.0)
+    plan = ra.plan_for_case(c)
+    desc = plan.describe()
+    say(f"case {c.name}: {desc}")
+    assert "halves=2" in desc and "MT=4" in desc and "KB=16" in desc
+    gpu = run_gpu(c, plan=plan)
+    plan.check()
+    ref = oracle_outputs(c)
+    err = np.abs(gpu[0].astype(np.float64) - ref[0])
+    bad = err > ATOL + RTOL * np.abs(ref[0])
+    if bad.any():
+        t = int(np.argwhere(bad)[0][0])
+        raise AssertionError(f"first step differing: {t} (max abs there {err[t].max():.3e})")
+    compare(c, gpu, ref, strict=True)
