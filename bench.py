@@ -151,7 +151,10 @@ def _pmc_rows(d, counter=False):
     import csv
     import glob
     rows = []
-    for fn in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+    files = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    if len(files) > 1:
+        raise SystemExit(f"several counter_collection.csv under {d} (one run per directory): {files}")
+    for fn in files:
         with open(fn, newline="") as f:
             for r in csv.DictReader(f):
                 v = float(r["Counter_Value"])
@@ -184,16 +187,24 @@ def counter_summary(d):
 
 
 def traffic_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, workload):
-    """Per-launch HBM bytes of each kernel: mean counter KiB per dispatch,
-    scaled by bytes / counter of the plain copy."""
+    """Per-launch HBM bytes of each kernel: mean counter KiB per dispatch over
+    the steady dispatches (each kernel's first one, with cold caches and
+    translation buffers, is left out when there are at least three), scaled
+    by bytes / counter of the plain copy."""
     import numpy as np
 
-    def per_kernel(d):
+    def per_kernel(d, first=None):
         acc = {}
         for name, did, v in _pmc_rows(d):
             acc.setdefault(name, {}).setdefault(did, 0.0)
             acc[name][did] += v
-        return {k: float(np.mean(list(v.values()))) for k, v in acc.items()}
+        out = {}
+        for k, v in acc.items():
+            vals = [v[i] for i in sorted(v)]
+            out[k] = float(np.mean(vals[1:] if len(vals) >= 3 else vals))
+            if first is not None:
+                first[k] = (vals[0], len(vals))
+        return out
 
     def copy_kib(d):
         pk = per_kernel(d)
@@ -203,7 +214,8 @@ def traffic_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, workload):
     cname, cf = copy_kib(cfetch_dir)
     _, cw = copy_kib(cwrite_dir)
     rscale, wscale = COPY_BYTES / (cf * 1024.0), COPY_BYTES / (cw * 1024.0)
-    fk, wk = per_kernel(fetch_dir), per_kernel(write_dir)
+    ff, fw = {}, {}
+    fk, wk = per_kernel(fetch_dir, ff), per_kernel(write_dir, fw)
     out = {"workload": workload, "copy_kernel": cname, "copy_fetch_kib": cf, "copy_write_kib": cw,
            "read_scale": rscale, "write_scale": wscale, "kernels": {}}
     for stage, prefix in KERNEL_NAMES.items():
@@ -214,6 +226,8 @@ def traffic_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, workload):
         f_kib, w_kib = fk[n], wk.get(n, float("nan"))
         out["kernels"][stage] = {
             "name": n, "fetch_kib": f_kib, "write_kib": w_kib,
+            "first_dispatch_fetch_kib": ff[n][0], "first_dispatch_write_kib": fw.get(n, (None,))[0],
+            "dispatches": ff[n][1],
             "traffic_bytes": f_kib * 1024.0 * rscale + w_kib * 1024.0 * wscale,
             "source_hash": kernel_hash(stage)}
     print(json.dumps(out, indent=1))

@@ -20,7 +20,7 @@
 // Tiling: 128x128 output tile per 256-thread workgroup, 4 waves of 64x64, K
 // staged through LDS in 128-byte row slices (32 fp32 or 64 bf16 values): the
 // next slice is loaded into registers while the current one is consumed and
-// replaces it between two barriers, so one LDS buffer (36 KiB) suffices and
+// replaces it between two barriers, so one LDS buffer (40 KiB) suffices and
 // three workgroups share a CU (measured faster than two double-buffered).  fp32 uses v_mfma_f32_16x16x4_f32, bf16 uses the gfx950
 // v_mfma_f32_16x16x32_bf16; for bf16, the chunk's X rows are first gathered
 // and rounded to bfloat16 (nearest even) once by gather_bf16_kernel.  Accumulation is in the
@@ -43,7 +43,7 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 128, BN = 128;
 constexpr int ROWB = 128;              // bytes of k per row per stage
-constexpr int LDSROW = ROWB + 16;      // padded LDS row stride (bytes)
+constexpr int LDSROW = ROWB + 32;      // padded LDS row stride (bytes): no bank conflicts
 constexpr int TILEB = BM * LDSROW;     // bytes of one operand tile in LDS
 
 __device__ __forceinline__ uint32_t bf16_bits(float f)
