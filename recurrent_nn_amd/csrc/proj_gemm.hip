@@ -147,60 +147,6 @@ __device__ __forceinline__ int64_t proj_dense(const ProjArgs &a, int64_t mc)
     return a.rowmap ? (int64_t)a.rowmap[mc] : mc;
 }
 
-// The rows the step loop reads in the chunk, step by step: step jl reads the
-// ranks r < na(j) (na(j) = rows with length > j; lengths by rank do not
-// increase), listed as jl * Bt + r.  One workgroup: 1024 steps at a time, the
-// counts by binary search, their exclusive scan, then the rows of each step
-// written by all threads.
-__global__ void __launch_bounds__(1024) proj_rows_kernel(ProjArgs a, int32_t *rowmap)
-{
-    __shared__ int32_t cnt[1024], off[1024];
-    const int tid = threadIdx.x;
-    int64_t base = 0;
-    for (int64_t s0 = 0; s0 < a.steps; s0 += 1024) {
-        const int64_t jl = s0 + tid;
-        int32_t na = 0;
-        if (jl < a.steps) {
-            const int64_t j = a.j_base + jl;
-            int lo = 0, hi = (int)a.Bt;                 // first rank whose length <= j
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (a.lens[a.rank_pos[mid]] > j)
-                    lo = mid + 1;
-                else
-                    hi = mid;
-            }
-            na = lo;
-        }
-        cnt[tid] = na;
-        off[tid] = na;
-        __syncthreads();
-        for (int o = 1; o < 1024; o <<= 1) {            // inclusive scan of the counts
-            const int32_t v = tid >= o ? off[tid - o] : 0;
-            __syncthreads();
-            off[tid] += v;
-            __syncthreads();
-        }
-        const int nsteps = (int)(a.steps - s0 < 1024 ? a.steps - s0 : 1024);
-        for (int k = 0; k < nsteps; ++k) {
-            const int64_t o = base + off[k] - cnt[k];
-            const int32_t first = (int32_t)((s0 + k) * a.Bt);
-            for (int r = tid; r < cnt[k]; r += 1024)
-                rowmap[o + r] = first + r;
-        }
-        base += off[nsteps - 1];
-        __syncthreads();                                 // before cnt and off are reused
-    }
-}
-
-int launch_proj_rows(const ProjArgs &a, int32_t *rowmap, void *stream)
-{
-    if (a.steps <= 0 || a.Bt <= 0)
-        return 0;
-    hipLaunchKernelGGL(proj_rows_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, a, rowmap);
-    return (int)hipGetLastError();
-}
-
 // bf16 projection: the chunk's computed X rows in order, rounded to
 // bfloat16 (nearest even) once, zeros for rows never read; the product then
 // reads bf16 rows directly instead of converting in every N tile.
