@@ -111,7 +111,11 @@ def achievable_peaks():
     device-to-device copy (HBM read + write), and torch's own fp32 and bf16
     matrix products at the plain shapes of the fp32 (S 512, Bt 64, I 1024,
     G*H*D 8192) and bf16 (S 256, Bt 256, I 2048, G*H 6144) projections, with
-    no row gather.  Context only: nothing on the measured path uses them."""
+    no row gather, in two operand layouts: the projection's own, X [M, K]
+    times W^T with W stored [N, K] ("_xwt"; W as the operator stores it), and
+    B stored [K, N].  The products write their input type (bf16 for the bf16
+    ones), where the projection writes fp32 XW.  Context only: nothing on the
+    measured path uses them."""
     import torch
     dev = torch.device("cuda:0")
 
@@ -139,7 +143,11 @@ def achievable_peaks():
         b = torch.randn(K, N, device=dev, generator=g).to(dt)      # [K, N], contiguous
         ms = ms_per(lambda: torch.matmul(a, b), 5)
         out[name] = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-        del a, b
+        del b
+        w = torch.randn(N, K, device=dev, generator=g).to(dt)      # [N, K], as W is stored
+        ms = ms_per(lambda: torch.mm(a, w.t()), 5)
+        out[name.replace("_tflops", "_xwt_tflops")] = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        del a, w
     out["spec"] = {"hbm_gbs": HBM_PEAK_GBS, "fp32_mfma_tflops": FP32_MFMA_PEAK_TFLOPS,
                    "bf16_mfma_tflops": BF16_MFMA_PEAK_TFLOPS}
     print(json.dumps(out), flush=True)
