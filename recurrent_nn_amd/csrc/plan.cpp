@@ -218,7 +218,7 @@ rnn_status choose_tiling(const rnn_attrs &a, rnn_plan &p)
         *res = resident_ok(p.NW, nt, *nta, p.phases, p.KB, p.MT, pairs);
         if (!*res && !streamed_ok(p.NW, nt, *nta, p.phases, pairs, p.MT))
             return false;
-        long lds = ((long)p.NW * p.BT * (nt * 16 + 4) + 3L * p.BT * u + 2L * p.BT + 11L * u) * 4;
+        long lds = ((long)p.NW * nt * 16 * (p.BT + 4) + 3L * p.BT * u + 2L * p.BT + 11L * u) * 4;
         if (lds > 160 * 1024)
             return false;
         *cost = (long)p.MT * nt * p.KB * 16 + (*res ? 0 : (long)p.MT * nt * p.KB * 4);

@@ -386,11 +386,12 @@ __device__ __forceinline__ float gru0_candidate(float xh, float rh, const float 
     return a1 + a2;
 }
 
-// LDS bytes of one workgroup: the four partial tiles, then the per-pair
-// states (h, c, z) and the per-row lengths.
+// LDS bytes of one workgroup: the waves' partial tiles (column-major, bt + 4
+// rows per column), then the per-pair states (h, c, z) and the per-row
+// lengths.
 __host__ __device__ inline size_t rec_lds_bytes(int nw, int bt, int nt, int u)
 {
-    return ((size_t)nw * bt * (nt * 16 + 4) + 3 * (size_t)bt * u + 2 * bt + 11 * (size_t)u) * 4;
+    return ((size_t)nw * nt * 16 * (bt + 4) + 3 * (size_t)bt * u + 2 * bt + 11 * (size_t)u) * 4;
 }
 
 // Depth (in 16-k blocks) of the A-operand prefetch of the register-resident
@@ -405,11 +406,14 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
     constexpr bool RES = KBR > 0;
     constexpr int BT = MT * 16;
     constexpr int NTC = NT * 16;
-    constexpr int LDR = NTC + 4;                 // LDS row stride of the partial tiles
+    constexpr int LDC = BT + 4;                  // column stride of the partial tiles (floats)
     constexpr int PH = TA > 0 ? 2 : 1;           // phases per step (2: GRU, linear_before_reset 0)
     extern __shared__ float smem[];
-    float *red = smem;                           // [kWaves][BT][LDR] partial tiles
-    float *hst = red + kWaves * BT * LDR;        // [BT * U] h of each (row, unit) pair
+    // partial tiles [kWaves][NTC][LDC], column-major: a lane's four rows of a
+    // column are contiguous (one 16-byte store per tile), and the gate
+    // arithmetic's reads of 16 units x 4 rows fall in distinct banks
+    float *red = smem;
+    float *hst = red + kWaves * NTC * LDC;       // [BT * U] h of each (row, unit) pair
     float *cst = hst + BT * a.U;                 // [BT * U] LSTM cell state
     float *zst = cst + BT * a.U;                 // [BT * U] GRU update gate between phases
     int *lst = (int *)(zst + BT * a.U);          // [BT] sequence length of each row
@@ -602,18 +606,16 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
             for (int nt = 0; nt < NT; ++nt) {
                 if (nt < t0 || nt >= t1)
                     continue;          // (uniform: the other phase's tiles)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    red[(w * BT + mt * 16 + 4 * lq + r) * LDR + nt * 16 + lr] = acc[mt][nt][r];
+                *(f4 *)(red + (w * NTC + nt * 16 + lr) * LDC + mt * 16 + 4 * lq) = acc[mt][nt];
             }
         __syncthreads();
         RNN_STAMP(q - a.q_begin, 2);
         auto rec_at = [&](int rl, int col) {
-            const float *p = red + rl * LDR + col;
+            const float *p = red + col * LDC + rl;
             float v = p[0];
 #pragma unroll
             for (int w2 = 1; w2 < NW; ++w2)
-                v = v + p[w2 * BT * LDR];             // fixed wave order
+                v = v + p[w2 * NTC * LDC];            // fixed wave order
             return v;
         };
 
@@ -681,7 +683,7 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
                 for (int g = 0; g < 4; ++g)
 #pragma unroll
                     for (int w2 = 0; w2 < kWaves; ++w2)
-                        part[n][g][w2] = g < G ? red[(w2 * BT + rl[n]) * LDR + g * uc + u[n]] : 0.0f;
+                        part[n][g][w2] = g < G ? red[(w2 * NTC + g * uc + u[n]) * LDC + rl[n]] : 0.0f;
 #pragma unroll
                 for (int e = 0; e < 11; ++e) {
                     const bool need = op == RNN_OP_RNN   ? (e == 0 || e == 4)
