@@ -52,6 +52,8 @@ def parse():
                    help="exact mode: k-ordered unfused products on the VALU (results bit-identical "
                         "to the oracle); reported against the fp32 vector peak")
     p.add_argument("--time-chunk", type=int, default=0, help="steps per time chunk (0: all)")
+    p.add_argument("--fuse-projection", type=int, default=0, choices=(0, 1, 2),
+                   help="0 automatic, 1 the projection as its own launch, 2 inside the step loop")
     p.add_argument("--peaks", action="store_true",
                    help="print library references (HBM copy, fp32/bf16 GEMM) and exit")
     p.add_argument("--copy-calibration", action="store_true",
@@ -319,7 +321,8 @@ def cpu_baseline(c, budget_s):
             "threads": nt, **hf, "seconds": dt}
 
 
-def measure(c, steps, warmup, dev, kernel_path=0, exact=False, time_chunk=0, stage_runs=None):
+def measure(c, steps, warmup, dev, kernel_path=0, exact=False, time_chunk=0, stage_runs=None,
+            fuse_projection=0):
     """Run one workload on the GPU: warm-up, exactly `steps` invocations
     between two events on the stream (the timed region), per-stage durations
     from the library's own events over further runs, and each invocation
@@ -334,7 +337,8 @@ def measure(c, steps, warmup, dev, kernel_path=0, exact=False, time_chunk=0, sta
     t = {k: (v.to(dev) if v is not None and k != "sequence_lens" else v)
          for k, v in c.tensors().items()}
     stream = torch.cuda.current_stream(dev)
-    with ra.plan_for_case(c, kernel_path=kernel_path, exact=exact, time_chunk=time_chunk) as plan:
+    with ra.plan_for_case(c, kernel_path=kernel_path, exact=exact, time_chunk=time_chunk,
+                          fuse_projection=fuse_projection) as plan:
         Y = torch.empty(plan.output_shapes()[0], dtype=torch.float32, device=dev)
         Yh = torch.empty(plan.output_shapes()[1], dtype=torch.float32, device=dev)
         Yc = torch.empty_like(Yh) if c.op == "LSTM" else None
@@ -391,12 +395,20 @@ def measure(c, steps, warmup, dev, kernel_path=0, exact=False, time_chunk=0, sta
             "min": each[0], "plan": desc}
 
 
+def plan_fused(m):
+    """Whether the measured plan computes the projection inside the step loop."""
+    return "fused=1" in m["plan"].split()
+
+
 def kernel_figures(c, m, exact=False):
     """Roofline figures of the projection and the step loop of one measured
     workload: achieved TFLOP/s and the fraction of the peak for the valid work
     (what the method computes) and for the nominal work (every step of every
-    row)."""
+    row).  A fused plan runs both products in the step loop: its figures
+    count both, and the projection has no launch of its own."""
     fl = flops_per_run(c)
+    if plan_fused(m):
+        fl = {k: (0.0, v[0] + v[1]) for k, v in fl.items()}
     proj_peak = BF16_MFMA_PEAK_TFLOPS if c.proj_bf16 else FP32_MFMA_PEAK_TFLOPS
     rec_peak = FP32_MFMA_PEAK_TFLOPS
     bound = "mfma"
@@ -407,6 +419,10 @@ def kernel_figures(c, m, exact=False):
     for i, (k, peak) in enumerate((("projection", proj_peak), ("recurrence", rec_peak))):
         ms = m["stage_ms"][k]
         fv, fn = fl["valid"][i], fl["nominal"][i]
+        if plan_fused(m) and k == "projection":
+            out[k] = {"fused": True, "ms": ms,
+                      "note": "computed inside the step loop (its FLOPs are counted there)"}
+            continue
         out[k] = {"bound": bound, "ms": ms, "peak": peak, "unit": "TFLOP/s",
                   "flop_valid": fv, "flop_nominal": fn,
                   "achieved": fv / (ms * 1e-3) / 1e12,
@@ -414,6 +430,8 @@ def kernel_figures(c, m, exact=False):
                   "achieved_nominal": fn / (ms * 1e-3) / 1e12,
                   "frac_nominal": fn / (ms * 1e-3) / 1e12 / peak}
     out["recurrence"]["us_per_step"] = m["stage_ms"]["recurrence"] * 1e3 / c.seq
+    if plan_fused(m):
+        out["recurrence"]["products"] = "projection + recurrent product (fused)"
     return out
 
 
@@ -435,7 +453,10 @@ def step_stamps(c, dev, kernel_path=0):
     the barrier, 4 gate arithmetic and stores issued, 5 this half's flag
     stored, from inside the next product); for the four-wave kernel each slot
     is a phase (0 start, 1 products issued, 2 partial tiles visible, 3 gate
-    arithmetic and stores issued, 4 next phase's flags seen)."""
+    arithmetic and stores issued, 4 next phase's flags seen).  With the
+    projection inside (fused), 5 is this half's flag stored from inside the
+    half's share of the next step's projections and 6 the end of that
+    share."""
     import numpy as np
     import torch
 
@@ -463,15 +484,24 @@ def step_stamps(c, dev, kernel_path=0):
         st = ws[off:off + nb].cpu().numpy().view(np.uint64).reshape(STAMP_SLOTS, STAMP_EVENTS)
         st = st.astype(np.int64)
         halves = desc["halves"] == "2"
+        fused = desc.get("fused") == "1"
         per_step = 2 if halves else int(desc["phases"])
         n = min(STAMP_SLOTS, c.seq * per_step)
         lo, hi = 2 * per_step, n - 2 * per_step          # steady slots
         rows = st[lo:hi]
         nxt = st[lo + 1:hi + 1, 0]
         names = (["wait_and_first_loads", "product", "partials_barrier", "gates_and_stores",
+                  "projection_share", "barrier_to_next_half"] if fused else
+                 ["wait_and_first_loads", "product", "partials_barrier", "gates_and_stores",
                   "to_next_half"] if halves else
                  ["product", "partials_barrier", "gates_and_stores", "handover_wait"])
-        if halves:
+        if fused:
+            # (event 5: this half's flag stored, from inside the projection
+            # share; 6: the share done)
+            iv = [rows[:, 1] - rows[:, 0], rows[:, 2] - rows[:, 1], rows[:, 3] - rows[:, 2],
+                  rows[:, 4] - rows[:, 3], rows[:, 6] - rows[:, 4], nxt - rows[:, 6]]
+            flag = rows[:, 5] - rows[:, 4]
+        elif halves:
             iv = [rows[:, 1] - rows[:, 0], rows[:, 2] - rows[:, 1], rows[:, 3] - rows[:, 2],
                   rows[:, 4] - rows[:, 3], nxt - rows[:, 4]]
             flag = rows[:, 5] - rows[:, 4]
@@ -535,7 +565,7 @@ def main():
     c = workloads.workload(args.workload)
     print(f"[bench] workload {c.name}: inputs drawn", file=sys.stderr, flush=True)
     m = measure(c, args.steps, args.warmup, dev, kernel_path=args.kernel_path, exact=args.exact,
-                time_chunk=args.time_chunk)
+                time_chunk=args.time_chunk, fuse_projection=args.fuse_projection)
     print(f"[bench] stage ms: {json.dumps(m['stage_ms'])}", file=sys.stderr, flush=True)
     kernels = kernel_figures(c, m, exact=args.exact)
     # size-derived rates of the step loop's operand streams (sizes over the
@@ -550,7 +580,8 @@ def main():
         "r_bytes_per_step": r_bytes, "r_gbs": r_bytes / t_step / 1e9,
         "r_frac_of_hbm": r_bytes / t_step / (HBM_PEAK_GBS * 1e9),
         "h_rows_read_bytes_per_step": h_bytes, "h_rows_read_gbs": h_bytes / t_step / 1e9}
-    dom = max(("projection", "recurrence"), key=lambda k: kernels[k]["ms"])
+    dom = "recurrence" if plan_fused(m) else max(("projection", "recurrence"),
+                                                 key=lambda k: kernels[k]["ms"])
     dk = kernels[dom]
     roofline = {"bound": dk["bound"], "achieved": round(dk["achieved"], 3), "peak": dk["peak"],
                 "unit": dk["unit"], "frac": round(dk["frac"], 4),
@@ -566,7 +597,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16+f32" if c.proj_bf16 else "f32",
         "data": "synthetic",
         "config": {"workload": c.name, "mode": "exact" if args.exact else "fast",
-                   "time_chunk": args.time_chunk, "op": c.op, "direction": c.direction, "seq": c.seq,
+                   "time_chunk": args.time_chunk, "fuse_projection": args.fuse_projection,
+                   "op": c.op, "direction": c.direction, "seq": c.seq,
                    "batch": c.batch, "input": c.input, "hidden": c.hidden, "dirs": c.dirs,
                    "layout": c.layout, "global_batch": c.batch, "seq_len": c.seq,
                    "parallelism": "none (1 GPU)", "plan": m["plan"]},
@@ -579,7 +611,7 @@ def main():
     }
     del c
     # ---- the other workloads of the list, same protocol, fewer runs ---------
-    if not args.no_configs and not args.exact and not args.time_chunk:
+    if not args.no_configs and not args.exact and not args.time_chunk and not args.fuse_projection:
         confs = {}
         for name in CONFIGS:
             if name == args.workload:

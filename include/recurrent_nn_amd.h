@@ -123,6 +123,16 @@ typedef struct rnn_attrs {
                                           binary64 method; results do not depend on the
                                           tiling and match that definition bit for bit.
                                           0 = fast mode (matrix-core products).           */
+    int32_t fuse_projection;           /* 0 or 1 = the input projection as its own launch
+                                          into a buffer of the workspace (the faster form
+                                          where both apply); 2 = the projection inside the
+                                          step loop, each workgroup computing the values of
+                                          its own gate columns and rows one step ahead from
+                                          its slice of W held in LDS, so that the workspace
+                                          holds no projections (needs the two-half schedule
+                                          in fast mode, an F32 projection, input_size a
+                                          multiple of 256 and the slice within LDS; else
+                                          InvalidInput).  Results are identical either way. */
 } rnn_attrs;
 
 /* Dimensions: hidden is R's last dimension, num_directions W's first. */

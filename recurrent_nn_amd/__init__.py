@@ -126,7 +126,7 @@ def make_attrs(op: str, direction: str = "forward", hidden_size: int = 0, layout
                constant_weights: bool = False, kernel_path: int = RNN_PATH_AUTO,
                units_per_block: int = 0, batch_tile: int = 0, waves_per_block: int = 0,
                barrier_spin_limit: int = 0, batch_halves: int = 0, time_chunk: int = 0,
-               exact: bool = False):
+               exact: bool = False, fuse_projection: int = 0):
     """Returns (attrs, keepalive); keep `keepalive` alive while attrs is used."""
     keep = []
     a = rnn_attrs()
@@ -164,6 +164,7 @@ def make_attrs(op: str, direction: str = "forward", hidden_size: int = 0, layout
     a.batch_halves = batch_halves
     a.time_chunk = time_chunk
     a.exact = 1 if exact else 0
+    a.fuse_projection = fuse_projection
     return a, keep
 
 

@@ -56,6 +56,7 @@ class rnn_attrs(ctypes.Structure):
         ("batch_halves", ctypes.c_int32),
         ("time_chunk", ctypes.c_int32),
         ("exact", ctypes.c_int32),
+        ("fuse_projection", ctypes.c_int32),
     ]
 
 

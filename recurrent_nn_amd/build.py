@@ -30,7 +30,7 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-ffp-contract=off",
 # kernel family and activation set (recurrence_inst.hip), so that they
 # compile in parallel.
 INST = "recurrence_inst.hip"
-INST_UNITS = [(fam, act) for fam in range(4) for act in range(5)]
+INST_UNITS = [(fam, act) for fam in range(5) for act in range(5)]
 
 # (source, extra flags, object name) of every translation unit: the .hip
 # files of csrc, the instantiation units, the HIP host code

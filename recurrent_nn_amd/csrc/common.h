@@ -96,6 +96,7 @@ struct rnn_plan {
     int32_t KB = 1;           // 16-wide k blocks per wave (Hp / (16 * NW))
     int32_t resident = 0;     // R slice held in registers across steps
     int32_t halves = 1;       // 2: each step as two half-batch sub-steps (rec_pipe_kernel)
+    int32_t fused = 0;        // 1: the projection computed inside the step loop (rec_fused_kernel)
     int32_t exact = 0;        // exact mode: k-ordered unfused products, exact activations
     int64_t Btp = 16;         // NBB * BT
     int32_t n_wg = 1;         // D * NBB * NUB
@@ -211,12 +212,16 @@ struct RecArgs {
     int32_t Hp, KB, NW, U, NUB, BT, NBB, MT, NTA, NTB, NT, phases;
     int32_t Btp;
     int32_t halves;         // 1, or 2 half-batch sub-steps per step (rec_pipe_kernel)
+    int32_t fused;          // 1: the projection inside the two-half step loop (rec_fused_kernel)
+    int32_t I;              // input size (the fused projection's k)
     int32_t exact;          // exact mode (rec_exact_kernel)
     int32_t reverse_only, layout, clip_on, input_forget, lbr;
     float clip;
     ActSpec act[2][3];
     // buffers
     const float *Rp, *XW, *B, *P;
+    // fused projection: X in the operator's layout, W packed [D][GH][I] (fp32)
+    const float *X, *Wp;
     // Position s holds batch row order[s] (identity when order is NULL) and
     // lens[s] is its length; each block of BT positions holds its rows in
     // order of decreasing length, so that the rows still active at a step
@@ -245,6 +250,8 @@ int launch_recurrence(const RecArgs &a, int resident, int persistent, void *stre
 int recurrence_can_persist(const RecArgs &a, int resident, int device, int *ok);
 bool recurrence_supported(int nw, int mt, int nt, int nta, int phases, int kb, int bt, int u,
                           int resident, int halves);
+// whether rec_fused_kernel takes a two-half tiling with this input size
+bool recurrence_fused_supported(int bt, int nt, int u, int64_t I);
 
 struct FinalArgs {
     const float *h0, *c0;

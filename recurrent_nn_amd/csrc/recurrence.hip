@@ -1,12 +1,13 @@
 // recurrence.hip -- selection and launch of the step-loop kernels
-// (recurrence_kernel.h, recurrence_pipe.h, recurrence_exact.h): the compiled
+// (recurrence_kernel.h, recurrence_pipe.h, recurrence_fused.h,
+// recurrence_exact.h): the compiled
 // shapes (tables in recurrence_inst.hip, one per kernel family and activation
 // set), the occupancy check of the persistent (cooperative) form, and the
 // launches.
 #include <hip/hip_runtime.h>
 
 #include "recurrence_exact.h"
-#include "recurrence_pipe.h"
+#include "recurrence_fused.h"
 
 namespace rnnamd {
 
@@ -14,7 +15,8 @@ namespace rnnamd {
     rec_fn rec_get_resident_a##A(int nw, int mt, int nt, int kb, int ta);                         \
     rec_fn rec_get_streamed2_a##A(int mt, int nt, int ta);                                        \
     rec_fn rec_get_streamed8_a##A(int mt, int nt, int ta);                                        \
-    rec_fn rec_get_pipe_a##A(int mth, int nt, int kb, int p);
+    rec_fn rec_get_pipe_a##A(int mth, int nt, int kb, int p);                                      \
+    rec_fn rec_get_fused_a##A(int mth, int nt, int kb, int p);
 RNN_DECL(0)
 RNN_DECL(1)
 RNN_DECL(2)
@@ -78,6 +80,17 @@ static rec_fn get_pipe(int act, int mth, int nt, int kb, int p)
     }
 }
 
+static rec_fn get_fused(int act, int mth, int nt, int kb, int p)
+{
+    switch (act) {
+    case 1: return rec_get_fused_a1(mth, nt, kb, p);
+    case 2: return rec_get_fused_a2(mth, nt, kb, p);
+    case 3: return rec_get_fused_a3(mth, nt, kb, p);
+    case 4: return rec_get_fused_a4(mth, nt, kb, p);
+    default: return rec_get_fused_a0(mth, nt, kb, p);
+    }
+}
+
 static rec_fn pick(const RecArgs &a, int resident)
 {
     if (a.exact) {  // exact mode: up to 128 columns per block
@@ -98,7 +111,13 @@ static rec_fn pick(const RecArgs &a, int resident)
         // phase, at most two pairs per thread and half
         const bool ok = resident && a.NW == 4 && a.phases == 1 && a.MT % 2 == 0 &&
                         (a.BT / 2) * a.U <= 2 * 256;
-        return ok ? get_pipe(act_set(a), a.MT / 2, a.NT, a.KB, ((a.BT / 2) * a.U + 255) / 256) : nullptr;
+        if (!ok)
+            return nullptr;
+        const int np = ((a.BT / 2) * a.U + 255) / 256;
+        if (a.fused)   // ... with the projection inside
+            return rec_fused_shape_ok(a.BT, a.NT, a.U, a.I) ? get_fused(act_set(a), a.MT / 2, a.NT, a.KB, np)
+                                                             : nullptr;
+        return get_pipe(act_set(a), a.MT / 2, a.NT, a.KB, np);
     }
     const int nthr = 64 * a.NW;
     const int np = (a.BT * a.U + nthr - 1) / nthr;
@@ -131,10 +150,17 @@ bool recurrence_supported(int nw, int mt, int nt, int nta, int phases, int kb, i
     return pick(a, resident) != nullptr;
 }
 
+bool recurrence_fused_supported(int bt, int nt, int u, int64_t I)
+{
+    return rec_fused_shape_ok(bt, nt, u, I);
+}
+
 static size_t rec_shmem(const RecArgs &a)
 {
     if (a.exact)
         return rec_exact_lds_bytes(a.BT, a.NT, a.U);
+    if (a.halves == 2 && a.fused)
+        return rec_fused_lds_bytes(a.BT, a.NT, a.U, a.I);
     return a.halves == 2 ? rec_pipe_lds_bytes(a.BT, a.NT, a.U) : rec_lds_bytes(a.NW, a.BT, a.NT, a.U);
 }
 

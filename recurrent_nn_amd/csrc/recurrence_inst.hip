@@ -1,18 +1,20 @@
 // recurrence_inst.hip -- the instantiation tables of the step-loop kernels
-// (recurrence_kernel.h, recurrence_pipe.h).  This one source is compiled once
-// per (kernel family RNN_FAMILY, activation set RNN_ACT), so that the twenty
-// tables build in parallel; the build passes both as -D definitions.
+// (recurrence_kernel.h, recurrence_pipe.h, recurrence_fused.h).  This one
+// source is compiled once per (kernel family RNN_FAMILY, activation set
+// RNN_ACT), so that the tables build in parallel; the build passes both as
+// -D definitions.
 //
 //   RNN_ACT: activation set compiled into the kernels -- 1 LSTM with
 //            Sigmoid/Tanh/Tanh, 2 GRU with HardSigmoid/Tanh, 3 RNN with Tanh,
 //            4 GRU with Sigmoid/Tanh, 0 any operator and set (run-time switch)
 //   RNN_FAMILY: 0 R resident in registers, 1 R streamed with up to 2 (row,
 //            unit) pairs per thread, 2 R streamed with up to 8 pairs, 3 two
-//            half-batch sub-steps per step (R resident)
-#include "recurrence_pipe.h"
+//            half-batch sub-steps per step (R resident), 4 the same with the
+//            input projection inside the step loop
+#include "recurrence_fused.h"
 
 #if !defined(RNN_ACT) || !defined(RNN_FAMILY)
-#error "compile with -DRNN_ACT=<0..4> -DRNN_FAMILY=<0..3>"
+#error "compile with -DRNN_ACT=<0..4> -DRNN_FAMILY=<0..4>"
 #endif
 
 #define RNN_CAT2(a, b) a##b
@@ -99,16 +101,23 @@ rec_fn RNN_CAT(RNN_NAME, RNN_ACT)(int mt, int nt, int ta)
 #undef P_
 #undef RNN_NAME
 
-#elif RNN_FAMILY == 3
+#elif RNN_FAMILY == 3 || RNN_FAMILY == 4
 // Two half-batch sub-steps: mth 16-row tiles per half (BT = 32 * mth), nt
 // 16-column tiles, kb 16-k blocks per wave (R slice of nt * kb * 4 registers
 // per lane), p pairs per thread and half (1 or 2).
-rec_fn RNN_CAT(rec_get_pipe_a, RNN_ACT)(int mth, int nt, int kb, int p)
+#if RNN_FAMILY == 3
+#define RNN_KERNEL rec_pipe_kernel
+#define RNN_NAME rec_get_pipe_a
+#else
+#define RNN_KERNEL rec_fused_kernel
+#define RNN_NAME rec_get_fused_a
+#endif
+rec_fn RNN_CAT(RNN_NAME, RNN_ACT)(int mth, int nt, int kb, int p)
 {
 #define RNN_P2(MTH_, NT_, KB_)                                                                    \
     if (mth == MTH_ && nt == NT_ && kb == KB_)                                                   \
-        return p == 1 ? rec_pipe_kernel<MTH_, NT_, KB_, RNN_ACT, 1>                              \
-                      : rec_pipe_kernel<MTH_, NT_, KB_, RNN_ACT, 2>;
+        return p == 1 ? RNN_KERNEL<MTH_, NT_, KB_, RNN_ACT, 1>                                   \
+                      : RNN_KERNEL<MTH_, NT_, KB_, RNN_ACT, 2>;
     RNN_P2(1, 1, 8)
     RNN_P2(1, 1, 16)
     RNN_P2(1, 2, 8)
@@ -120,6 +129,8 @@ rec_fn RNN_CAT(rec_get_pipe_a, RNN_ACT)(int mth, int nt, int kb, int p)
 #undef RNN_P2
     return nullptr;
 }
+#undef RNN_KERNEL
+#undef RNN_NAME
 #endif
 
 }  // namespace rnnamd

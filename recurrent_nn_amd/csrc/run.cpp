@@ -68,6 +68,8 @@ RecArgs rec_args(const rnn_plan &p, unsigned char *ws, const float *B, const flo
     r.phases = p.phases;
     r.Btp = (int32_t)p.Btp;
     r.halves = p.halves;
+    r.fused = p.fused;
+    r.I = (int32_t)p.I;
     r.exact = p.exact;
     r.reverse_only = p.reverse_only;
     r.layout = p.layout;
@@ -77,6 +79,7 @@ RecArgs rec_args(const rnn_plan &p, unsigned char *ws, const float *B, const flo
     r.lbr = p.lbr;
     std::memcpy(r.act, p.act, sizeof(r.act));
     r.Rp = (const float *)(ws + p.ws.rp);
+    r.Wp = (const float *)(ws + p.ws.wp);
     r.XW = (const float *)(ws + p.ws.xw);
     r.B = B;
     r.P = P;
@@ -355,50 +358,54 @@ rnn_status run_enqueue(rnn_plan *p, hipStream_t s, void *workspace, const float 
     const int64_t nchunks = (p->S + p->C - 1) / p->C;
     RecArgs ra = rec_args(*p, ws, B, P, Y, Y_h, Y_c);
     ra.order = order_dev;
+    ra.X = X;
     for (int64_t ck = 0; ck < nchunks; ++ck) {
         const int64_t j0 = ck * p->C, j1 = std::min<int64_t>(p->S, j0 + p->C);
         if (ck == 0)
             tm.begin(STAGE_PROJ);
-        ProjArgs pr{};
-        pr.X = X;
-        pr.Xb = (uint16_t *)(ws + p->ws.xb);
-        pr.Wp = ws + p->ws.wp;
-        pr.XW = (float *)(ws + p->ws.xw);
-        pr.K = p->I;
-        pr.S = p->S;
-        pr.Bt = p->Bt;
-        pr.GH = (int64_t)p->G * p->H;
-        pr.D = p->D;
-        pr.steps = p->C;
-        pr.j_base = j0;
-        pr.lens = lens_dev;
-        pr.order = order_dev;
-        pr.rank_pos = order_dev ? order_dev + p->Bt : nullptr;
-        // With sequence_lens and a product of many tiles, only the rows the
-        // step loop reads in this chunk, listed on the device (for a small
-        // product the extra launch costs more than the rows it saves, and
-        // whole tiles with no row read are skipped anyway).
-        pr.m_rows = p->C * p->Bt;
-        const int64_t dense_tiles = p->D * ((p->C * p->Bt + 127) / 128) * ((pr.GH + 127) / 128);
-        const bool row_list = sequence_lens && (p->proj_rows == 1 ||
-                                                (p->proj_rows == 0 && dense_tiles >= 2048));
-        if (row_list) {
-            pr.m_rows = 0;
-            for (int64_t b = 0; b < p->Bt; ++b)
-                pr.m_rows += std::min<int64_t>(p->C, std::max<int64_t>(0, sequence_lens[b] - j0));
-            int32_t *rowmap = (int32_t *)(ws + p->ws.rowmap);
-            pr.rowmap = rowmap;
-            rc = launch_proj_rows(pr, rowmap, s);
+        // (a fused plan: the step loop computes the projections itself)
+        if (!p->fused) {
+            ProjArgs pr{};
+            pr.X = X;
+            pr.Xb = (uint16_t *)(ws + p->ws.xb);
+            pr.Wp = ws + p->ws.wp;
+            pr.XW = (float *)(ws + p->ws.xw);
+            pr.K = p->I;
+            pr.S = p->S;
+            pr.Bt = p->Bt;
+            pr.GH = (int64_t)p->G * p->H;
+            pr.D = p->D;
+            pr.steps = p->C;
+            pr.j_base = j0;
+            pr.lens = lens_dev;
+            pr.order = order_dev;
+            pr.rank_pos = order_dev ? order_dev + p->Bt : nullptr;
+            // With sequence_lens and a product of many tiles, only the rows the
+            // step loop reads in this chunk, listed on the device (for a small
+            // product the extra launch costs more than the rows it saves, and
+            // whole tiles with no row read are skipped anyway).
+            pr.m_rows = p->C * p->Bt;
+            const int64_t dense_tiles = p->D * ((p->C * p->Bt + 127) / 128) * ((pr.GH + 127) / 128);
+            const bool row_list = sequence_lens && (p->proj_rows == 1 ||
+                                                    (p->proj_rows == 0 && dense_tiles >= 2048));
+            if (row_list) {
+                pr.m_rows = 0;
+                for (int64_t b = 0; b < p->Bt; ++b)
+                    pr.m_rows += std::min<int64_t>(p->C, std::max<int64_t>(0, sequence_lens[b] - j0));
+                int32_t *rowmap = (int32_t *)(ws + p->ws.rowmap);
+                pr.rowmap = rowmap;
+                rc = launch_proj_rows(pr, rowmap, s);
+                if (rc)
+                    return hip_fail((hipError_t)rc, "projection rows");
+            }
+            pr.reverse_only = p->reverse_only;
+            pr.layout = p->layout;
+            pr.bf16 = p->proj_bf16;
+            pr.exact = p->exact;
+            rc = launch_projection(pr, s);
             if (rc)
-                return hip_fail((hipError_t)rc, "projection rows");
+                return hip_fail((hipError_t)rc, "projection");
         }
-        pr.reverse_only = p->reverse_only;
-        pr.layout = p->layout;
-        pr.bf16 = p->proj_bf16;
-        pr.exact = p->exact;
-        rc = launch_projection(pr, s);
-        if (rc)
-            return hip_fail((hipError_t)rc, "projection");
         if (ck == 0) {
             tm.end(STAGE_PROJ);
             tm.begin(STAGE_REC);

@@ -163,10 +163,17 @@ def test_cell_run_errors_before_any_device_work():
 
 
 def test_time_chunks_shrink_the_workspace_and_lift_the_scratch_limit():
-    full = ra.RNNPlan("LSTM", 512, 64, 1024, 1024, direction="bidirectional")
-    ch = ra.RNNPlan("LSTM", 512, 64, 1024, 1024, direction="bidirectional", time_chunk=64)
+    # (the projections held in the workspace: a separate projection launch)
+    full = ra.RNNPlan("LSTM", 512, 64, 1024, 1024, direction="bidirectional", fuse_projection=1)
+    ch = ra.RNNPlan("LSTM", 512, 64, 1024, 1024, direction="bidirectional", time_chunk=64,
+                    fuse_projection=1)
     assert "C=512" in full.describe() and "C=64" in ch.describe()
     assert ch.workspace_bytes < full.workspace_bytes / 4
+    # the projection inside the step loop holds no projections at all
+    fused = ra.RNNPlan("LSTM", 512, 64, 1024, 1024, direction="bidirectional", fuse_projection=2)
+    assert "fused=1" in fused.describe() and "fused=0" in full.describe()
+    xw = 2 * 512 * 64 * 4096 * 4
+    assert fused.workspace_bytes <= full.workspace_bytes - xw
     # a chunk at least as long as the sequence is the whole sequence
     assert "C=20" in ra.RNNPlan("GRU", 20, 4, 8, 16, time_chunk=50).describe()
     # 2^22 steps x 64 rows x 4 gates x 64 units exceeds 2^30 floats at once,
@@ -182,9 +189,10 @@ def test_time_chunks_shrink_the_workspace_and_lift_the_scratch_limit():
 
 def test_workspace_and_tiling_of_the_named_workloads():
     expect = {
-        "lstm_bidir_s512_b64_i1024_h1024": dict(resident="1", workgroups="256"),
+        "lstm_bidir_s512_b64_i1024_h1024": dict(resident="1", workgroups="256", halves="2",
+                                                fused="0"),
         "gru_rev_s256_b256_i2048_h2048_bf16": dict(workgroups="256", NBB="2", BT="128", U="16"),
-        "gru_fwd_s128_b32_i256_h512_lbr0": dict(phases="2"),
+        "gru_fwd_s128_b32_i256_h512_lbr0": dict(phases="2", fused="0"),
     }
     for name, want in expect.items():
         c = workloads.Case(*[None] * 6)
@@ -198,8 +206,35 @@ def test_workspace_and_tiling_of_the_named_workloads():
         desc = dict(kv.split("=") for kv in p.describe().split())
         for k, v in want.items():
             assert desc[k] == v, (name, k, desc[k])
-        assert p.workspace_bytes >= S * Bt * (2 if d == "bidirectional" else 1) * \
-            {"LSTM": 4, "GRU": 3}[op] * H * 4        # XW is materialised
+        xw = S * Bt * (2 if d == "bidirectional" else 1) * {"LSTM": 4, "GRU": 3}[op] * H * 4
+        if desc["fused"] == "1":      # the projections never leave the step loop
+            assert p.workspace_bytes < xw
+        else:                         # XW is materialised
+            assert p.workspace_bytes >= xw
+
+
+def test_fused_projection_needs_its_shape():
+    # on request where the two-half schedule, an fp32 projection, I in whole
+    # 256-input ranges and the W slice in LDS allow it (never automatic);
+    # elsewhere the request is an InvalidInput
+    assert "fused=0" in ra.RNNPlan("GRU", 6, 50, 256, 500, linear_before_reset=1).describe()
+    assert "fused=1" in ra.RNNPlan("GRU", 6, 50, 256, 500, linear_before_reset=1,
+                                   fuse_projection=2).describe()
+    for kw in (dict(), dict(proj_bf16=True), dict(exact=True), dict(batch_halves=1)):
+        I = 40 if not kw else 1024
+        p = ra.RNNPlan("LSTM", 3, 64, I, 1024, **kw)
+        assert "fused=0" in p.describe(), kw
+        with pytest.raises(ra.RNNError) as ei:
+            ra.RNNPlan("LSTM", 3, 64, I, 1024, fuse_projection=2, **kw)
+        assert ei.value.status == ra.RNN_ERR_INVALID_INPUT
+    # the W slice of 32 gate columns over 2048 inputs does not fit in LDS
+    with pytest.raises(ra.RNNError):
+        ra.RNNPlan("LSTM", 3, 64, 2048, 1024, direction="bidirectional", fuse_projection=2)
+    assert "fused=1" in ra.RNNPlan("LSTM", 3, 64, 2048, 1024, fuse_projection=2).describe()
+    # off on request; out of range
+    assert "fused=0" in ra.RNNPlan("LSTM", 3, 64, 1024, 1024, fuse_projection=1).describe()
+    with pytest.raises(ra.RNNError):
+        ra.RNNPlan("LSTM", 3, 64, 1024, 1024, fuse_projection=3)
 
 
 def test_zero_size_plans_need_no_workspace():

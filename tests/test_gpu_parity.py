@@ -441,27 +441,31 @@ def test_resident_kernels_without_bias_match_oracle(op, attrs):
     compare(c, run_gpu(c))
 
 
-@pytest.mark.parametrize("halves", [1, 2])
-def test_a_stalled_barrier_raises_the_device_error_and_the_kernel_exits(halves, monkeypatch):
+@pytest.mark.parametrize("halves,inp", [(1, 16), (2, 16), (2, 512)])
+def test_a_stalled_barrier_raises_the_device_error_and_the_kernel_exits(halves, inp, monkeypatch):
     # Forced from the host: with RNN_AMD_TEST_WITHHOLD_FLAGS the step loops
     # never store their flags, so every wait between steps runs out its spin
     # limit (1: two polls); the kernel then runs on without waiting and exits
-    # normally, and rnn_workspace_check reports the error it raised.
-    c = workloads.random_case("LSTM", "bidirectional", 8, 64, 16, 1024, seed=3, with_h0=True,
-                              scale=1.0 / 32)
+    # normally, and rnn_workspace_check reports the error it raised.  (Input
+    # size 512: the two-half kernel with the projection inside.)
+    c = workloads.random_case("LSTM", "bidirectional", 8, 64, inp, 1024, seed=3, with_h0=True,
+                              scale=1.0 / 32, x_scale=4.0 / inp ** 0.5)
     say(f"case {c.name} with withheld flags, barrier_spin_limit=1, batch_halves={halves}")
     monkeypatch.setenv("RNN_AMD_TEST_WITHHOLD_FLAGS", "1")
+    fuse = 2 if inp == 512 else 0
     plan = ra.plan_for_case(c, kernel_path=ra.RNN_PATH_PERSISTENT, barrier_spin_limit=1,
-                            batch_halves=halves)
+                            batch_halves=halves, fuse_projection=fuse)
     monkeypatch.delenv("RNN_AMD_TEST_WITHHOLD_FLAGS")
     assert "workgroups=256" in plan.describe() and f"halves={halves}" in plan.describe()
+    assert ("fused=1" in plan.describe()) == (inp == 512)
     ra.run_case(c, plan=plan)
     torch.cuda.synchronize()
     with pytest.raises(ra.RNNError) as ei:
         plan.check()
     assert ei.value.status == ra.RNN_ERR_DEVICE
     # a plan made without the switch, on the same inputs, is clean and matches the oracle
-    plan2 = ra.plan_for_case(c, kernel_path=ra.RNN_PATH_PERSISTENT, batch_halves=halves)
+    plan2 = ra.plan_for_case(c, kernel_path=ra.RNN_PATH_PERSISTENT, batch_halves=halves,
+                             fuse_projection=fuse)
     out = ra.run_case(c, plan=plan2)
     torch.cuda.synchronize()
     plan2.check()
