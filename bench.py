@@ -446,7 +446,7 @@ def rounded(d):
 STAMP_SLOTS, STAMP_EVENTS = 1024, 8       # recurrent_nn_amd/csrc/common.h
 
 
-def step_stamps(c, dev, kernel_path=0):
+def step_stamps(c, dev, kernel_path=0, fuse_projection=0):
     """Cycle stamps of the instrumented build: for the two-half kernel each
     slot is a half-step (events: 0 half start, 1 product start after the flag
     wait and the first loads, 2 products issued, 3 partial tiles visible after
@@ -464,7 +464,7 @@ def step_stamps(c, dev, kernel_path=0):
 
     t = {k: (v.to(dev) if v is not None and k != "sequence_lens" else v)
          for k, v in c.tensors().items()}
-    with ra.plan_for_case(c, kernel_path=kernel_path) as plan:
+    with ra.plan_for_case(c, kernel_path=kernel_path, fuse_projection=fuse_projection) as plan:
         desc = dict(kv.split("=", 1) for kv in plan.describe().split() if "=" in kv)
         off = int(desc.get("stamps", "0"))
         if not off:
@@ -558,7 +558,7 @@ def main():
     if args.stamps:
         torch.cuda.set_device(0)
         print(json.dumps(step_stamps(workloads.workload(args.workload), torch.device("cuda:0"),
-                                     args.kernel_path)), flush=True)
+                                     args.kernel_path, args.fuse_projection)), flush=True)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -585,7 +585,8 @@ def main():
     dk = kernels[dom]
     roofline = {"bound": dk["bound"], "achieved": round(dk["achieved"], 3), "peak": dk["peak"],
                 "unit": dk["unit"], "frac": round(dk["frac"], 4),
-                "traffic": measured_traffic(c.name, dom), "kernel": dom,
+                # (the recorded counters are those of the separate kernels)
+                "traffic": None if plan_fused(m) else measured_traffic(c.name, dom), "kernel": dom,
                 "work": "valid (sum of sequence lengths x directions steps)"}
 
     ms = m["ms"]
