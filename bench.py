@@ -74,9 +74,13 @@ def parse():
 
 
 # Source files whose kernels a traffic figure was measured on; a figure whose
-# hash no longer matches the tree is stale and not reported.
+# hash no longer matches the tree is stale and not reported.  The fast step
+# loops (the two-half and four-wave kernels) are compiled from the
+# instantiation source and the headers below; the exact-mode and fused
+# kernels and the launcher are not part of them.
 KERNEL_SOURCES = {
-    "recurrence": ["activations.h", "common.h"],     # + every recurrence* file
+    "recurrence": ["activations.h", "common.h", "recurrence_kernel.h", "recurrence_pipe.h",
+                   "recurrence_inst.hip"],
     "projection": ["proj_gemm.hip", "common.h"],
 }
 KERNEL_NAMES = {"recurrence": "rec_", "projection": "proj_gemm"}
@@ -88,8 +92,6 @@ def kernel_hash(stage):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "recurrent_nn_amd", "csrc")
     names = list(KERNEL_SOURCES[stage])
-    if stage == "recurrence":
-        names += sorted(f for f in os.listdir(csrc) if f.startswith("recurrence"))
     for n in names:
         with open(os.path.join(csrc, n), "rb") as f:
             h.update(n.encode() + b"\0" + f.read())

@@ -93,16 +93,13 @@ static rec_fn get_fused(int act, int mth, int nt, int kb, int p)
 
 static rec_fn pick(const RecArgs &a, int resident)
 {
-    if (a.exact) {  // exact mode: up to 128 columns per block
-        if (a.NT * 16 > 128)
+    if (a.exact) {  // exact mode: up to 128 columns and 64 rows per block
+        if (a.NT * 16 > 128 || a.BT > 64 || a.Hp % kExactKT != 0)
             return nullptr;
         switch (rec_exact_nacc(a.BT, a.NT * 16)) {
         case 1: return rec_exact_kernel<1>;
         case 2: return rec_exact_kernel<2>;
         case 4: return rec_exact_kernel<4>;
-        case 8: return rec_exact_kernel<8>;
-        case 16: return rec_exact_kernel<16>;
-        case 32: return rec_exact_kernel<32>;
         default: return nullptr;
         }
     }

@@ -26,11 +26,11 @@
 
 namespace rnnamd {
 
-constexpr int kExactKT = 32;        // k values per staged chunk (Hp is a multiple)
+constexpr int kExactKT = 64;         // k values per staged chunk (Hp, a multiple of 64, is a multiple)
 constexpr int kExactKTP = kExactKT + 4;   // LDS row stride (floats)
-// Threads per workgroup: eight waves, two per SIMD, so that one wave's LDS
-// and dependency waits are covered by the other's arithmetic.
-constexpr int kExactThreads = 512;
+// Threads per workgroup: sixteen waves, four per SIMD, so that one wave's LDS
+// and dependency waits are covered by the others' arithmetic.
+constexpr int kExactThreads = 1024;
 
 // LDS bytes: H chunk [BT][KTP], R chunk [NTC][KTP], the sums [BT][NTC],
 // then h, c, z per pair, lengths, per-unit constants.
@@ -43,8 +43,8 @@ __host__ __device__ inline size_t rec_exact_lds_bytes(int bt, int nt, int u)
 
 // Rows per thread for a block of bt rows and ntc columns (two columns per
 // thread, kExactThreads threads): the rows per pass rpp = kExactThreads /
-// (ntc / 2), and ceil(bt / rpp)
-// rounded up to a power of two.
+// (ntc / 2), and ceil(bt / rpp) rounded up to a power of two (at most 4 for
+// the blocks exact mode takes: bt <= 64, ntc <= 128).
 __host__ __device__ inline int rec_exact_nacc(int bt, int ntc)
 {
     const int rpp = kExactThreads / (ntc / 2);
@@ -137,8 +137,8 @@ __global__ void __launch_bounds__(kExactThreads, 1) rec_exact_kernel(RecArgs a)
     const bool worker = r0 < rpp;
     // staging: H chunk = BT rows x KT/4 float4, R chunk = ncol rows x KT/4
     constexpr int Q = KT / 4;                    // float4 per row and chunk
-    constexpr int SH = 64 * Q / kExactThreads;   // H float4 per thread (BT <= 64)
-    constexpr int SR = 128 * Q / kExactThreads;  // R float4 per thread (ncol <= 128)
+    constexpr int SH = (64 * Q + kExactThreads - 1) / kExactThreads;    // H float4 per thread (BT <= 64)
+    constexpr int SR = (128 * Q + kExactThreads - 1) / kExactThreads;   // R float4 per thread (ncol <= 128)
     const int nchunks = Hp / KT;
 
     bool dead = false;
