@@ -75,12 +75,11 @@ def parse():
 
 # Source files whose kernels a traffic figure was measured on; a figure whose
 # hash no longer matches the tree is stale and not reported.  The fast step
-# loops (the two-half and four-wave kernels) are compiled from the
-# instantiation source and the headers below; the exact-mode and fused
-# kernels and the launcher are not part of them.
+# loops (the two-half and four-wave kernels) are defined in the headers
+# below; the exact-mode and fused kernels, the launcher and the tables that
+# pick instantiations are not part of them.
 KERNEL_SOURCES = {
-    "recurrence": ["activations.h", "common.h", "recurrence_kernel.h", "recurrence_pipe.h",
-                   "recurrence_inst.hip"],
+    "recurrence": ["activations.h", "common.h", "recurrence_kernel.h", "recurrence_pipe.h"],
     "projection": ["proj_gemm.hip", "common.h"],
 }
 KERNEL_NAMES = {"recurrence": "rec_", "projection": "proj_gemm"}

@@ -104,7 +104,8 @@ rec_fn RNN_CAT(RNN_NAME, RNN_ACT)(int mt, int nt, int ta)
 #elif RNN_FAMILY == 3 || RNN_FAMILY == 4
 // Two half-batch sub-steps: mth 16-row tiles per half (BT = 32 * mth), nt
 // 16-column tiles, kb 16-k blocks per wave (R slice of nt * kb * 4 registers
-// per lane), p pairs per thread and half (1 or 2).
+// per lane), p pairs per thread and half: 1 (R resident allows at most two
+// pairs per thread over the whole tile, so one per half).
 #if RNN_FAMILY == 3
 #define RNN_KERNEL rec_pipe_kernel
 #define RNN_NAME rec_get_pipe_a
@@ -115,9 +116,8 @@ rec_fn RNN_CAT(RNN_NAME, RNN_ACT)(int mt, int nt, int ta)
 rec_fn RNN_CAT(RNN_NAME, RNN_ACT)(int mth, int nt, int kb, int p)
 {
 #define RNN_P2(MTH_, NT_, KB_)                                                                    \
-    if (mth == MTH_ && nt == NT_ && kb == KB_)                                                   \
-        return p == 1 ? RNN_KERNEL<MTH_, NT_, KB_, RNN_ACT, 1>                                   \
-                      : RNN_KERNEL<MTH_, NT_, KB_, RNN_ACT, 2>;
+    if (mth == MTH_ && nt == NT_ && kb == KB_ && p == 1)                                         \
+        return RNN_KERNEL<MTH_, NT_, KB_, RNN_ACT, 1>;
     RNN_P2(1, 1, 8)
     RNN_P2(1, 1, 16)
     RNN_P2(1, 2, 8)

@@ -3,7 +3,8 @@ bit-identical to the separate projection launch (fuse_projection = 1) on
 every output, and within the fp32 bars of the oracle.  The cases cover both
 places the flag of a half goes out (inside the projection for input sizes
 of 512 and more, from the next recurrent product at 256), batch tiles of 64
-and 32 (with one column tile, two waves hold no projection tile), sequence
+and 32 (with one column tile two waves hold no projection tile, with two
+each wave holds one), sequence
 lengths in both directions, layout 1, ragged batch and hidden, the compiled
 and run-time activation sets, time chunks and one launch per step."""
 import hashlib
@@ -43,11 +44,15 @@ FUSED = [
     # a set compiled through the run-time switch, input_forget, I = 1024
     dict(op="LSTM", direction="forward", S=5, Bt=33, I=1024, H=480, input_forget=1,
          activations=["HardSigmoid", "Softsign", "Tanh"], alpha=[0.3], beta=[0.5]),
+    # batch tile 32 with two column tiles: each wave one projection tile
+    dict(op="LSTM", direction="reverse", S=5, Bt=24, I=512, H=512, with_lens=True,
+         plan=dict(units_per_block=8)),
 ]
 
 
 def _case(k):
     spec = dict(FUSED[k])
+    spec.pop("plan", None)
     op, direction = spec.pop("op"), spec.pop("direction")
     S, Bt, I, H = spec.pop("S"), spec.pop("Bt"), spec.pop("I"), spec.pop("H")
     lay = spec.pop("layout", 0)
@@ -60,12 +65,13 @@ def _case(k):
 @pytest.mark.parametrize("k", range(len(FUSED)))
 def test_fused_projection_matches_separate_launch_bitwise_and_the_oracle(k):
     c = _case(k)
+    pk = FUSED[k].get("plan", {})
     say(f"case {c.name} {FUSED[k]}")
-    desc = ra.plan_for_case(c, fuse_projection=2).describe()
+    desc = ra.plan_for_case(c, fuse_projection=2, **pk).describe()
     say(f"  plan {desc}")
     assert "fused=1" in desc and "halves=2" in desc
-    fused = run_gpu(c, fuse_projection=2)
-    sep = run_gpu(c, fuse_projection=1)
+    fused = run_gpu(c, fuse_projection=2, **pk)
+    sep = run_gpu(c, fuse_projection=1, **pk)
     assert _digest(fused) == _digest(sep)
     compare(c, fused, strict=True)
     if k == 0:
