@@ -21,7 +21,7 @@ ACTS = ["Relu", "Tanh", "Sigmoid", "Affine", "LeakyRelu", "ThresholdedRelu", "Sc
 BOUNDED = ["Tanh", "Sigmoid", "HardSigmoid", "Softsign", "ScaledTanh"]
 
 
-def _configs(n=40, seed=2026):
+def _configs(n=100, seed=2026):
     rng = np.random.default_rng(seed)
     out = []
     for k in range(n):
