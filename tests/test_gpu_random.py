@@ -2,9 +2,11 @@
 layout, shapes (ragged batch and hidden sizes, input sizes that are and are
 not whole projection stages), sequence lengths, bias, peepholes, clip,
 input_forget, linear_before_reset, activation sets with their alpha/beta
-cursors, and the run options (exact mode, the projection inside the step
-loop where the shape allows it, time chunks, one launch per step).  Fast
-mode is held to the fp32 bars, exact mode to bit equality."""
+cursors, the bf16 projection, and the run options (exact mode, the
+projection inside the step loop where the shape allows it, time chunks, one
+launch per step).  Fast mode is held to the fp32 bars (against the oracle
+with the same bf16 rounding of X and W where the projection is bf16), exact
+mode to bit equality."""
 import numpy as np
 import pytest
 
@@ -53,6 +55,7 @@ def _configs(n=100, seed=2026):
             cfg["activations"] = names
             cfg["alpha"] = [float(a) for a in rng.uniform(0.1, 1.2, size=3)]
             cfg["beta"] = [float(b) for b in rng.uniform(0.1, 0.9, size=2)]
+        cfg["proj_bf16"] = bool(rng.integers(5) == 0)
         cfg["time_chunk"] = int(rng.choice([0, 0, 2, 3]))
         cfg["kernel_path"] = int(rng.choice([0, 0, 0, 2]))
         cfg["fuse"] = bool(rng.integers(4) > 0)
