@@ -75,22 +75,29 @@ def parse():
 
 # Source files whose kernels a traffic figure was measured on; a figure whose
 # hash no longer matches the tree is stale and not reported.  The fast step
-# loops (the two-half and four-wave kernels) are defined in the headers
-# below; the exact-mode and fused kernels, the launcher and the tables that
-# pick instantiations are not part of them.
+# loops are defined in the headers below (the four-wave kernel in
+# recurrence_kernel.h, the two-half kernel also in recurrence_pipe.h); the
+# exact-mode and fused kernels, the launcher and the tables that pick
+# instantiations are not part of them.
 KERNEL_SOURCES = {
-    "recurrence": ["activations.h", "common.h", "recurrence_kernel.h", "recurrence_pipe.h"],
+    "recurrence": ["activations.h", "common.h", "recurrence_kernel.h"],
     "projection": ["proj_gemm.hip", "common.h"],
 }
+KERNEL_EXTRA_SOURCES = {"rec_pipe_kernel": ["recurrence_pipe.h"]}
 KERNEL_NAMES = {"recurrence": "rec_", "projection": "proj_gemm"}
 COPY_BYTES = 1 << 30
 
 
-def kernel_hash(stage):
+def kernel_hash(stage, kernel_name=""):
+    """Hash of the sources of a stage's kernel (kernel_name: the measured
+    kernel's name, which adds the sources of its own form)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "recurrent_nn_amd", "csrc")
     names = list(KERNEL_SOURCES[stage])
+    for key, extra in KERNEL_EXTRA_SOURCES.items():
+        if key in kernel_name:
+            names += extra
     for n in names:
         with open(os.path.join(csrc, n), "rb") as f:
             h.update(n.encode() + b"\0" + f.read())
@@ -240,7 +247,7 @@ def traffic_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, workload):
             "first_dispatch_fetch_kib": ff[n][0], "first_dispatch_write_kib": fw.get(n, (None,))[0],
             "dispatches": ff[n][1],
             "traffic_bytes": f_kib * 1024.0 * rscale + w_kib * 1024.0 * wscale,
-            "source_hash": kernel_hash(stage)}
+            "source_hash": kernel_hash(stage, n)}
     print(json.dumps(out, indent=1))
 
 
@@ -253,7 +260,7 @@ def measured_traffic(workload, stage):
             k = json.load(f)["kernels"][stage]
     except (OSError, KeyError, ValueError):
         return None
-    if k.get("source_hash") != kernel_hash(stage):
+    if k.get("source_hash") != kernel_hash(stage, k.get("name", "")):
         return None
     return k["traffic_bytes"]
 

@@ -334,12 +334,21 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
                     xw[k][g] = xw_next[h][k][g];
+            // (the next step's row is loaded whether or not the pair is still
+            // active there: an inactive pair's gate results are discarded,
+            // and the row lies inside the chunk's XW either way)
             auto prefetch_xw = [&]() {
                 if (q + 1 < a.q_end) {
+                    const float *base = a.XW + (size_t)(q + 1 - a.j_base) * xstep;
 #pragma unroll
                     for (int k = 0; k < P; ++k)
-                        if (pk[h][k] >= 0)
-                            fetch_xw_q(q + 1, h, k, xw_next[h][k]);
+                        if (pk[h][k] >= 0) {
+                            const float *src = base + xoff[h][k];
+#pragma unroll
+                            for (int g = 0; g < 4; ++g)
+                                if (g < G)
+                                    xw_next[h][k][g] = src[g * uc];
+                        }
                 }
             };
 

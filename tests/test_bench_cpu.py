@@ -73,7 +73,8 @@ def test_traffic_summary_scales_steady_dispatches_by_the_copy(tmp_path, capsys):
     assert r["fetch_kib"] == 200.0 and r["write_kib"] == 20.0
     assert r["first_dispatch_fetch_kib"] == 900.0 and r["dispatches"] == 3
     assert r["traffic_bytes"] == pytest.approx((200.0 * 2 + 20.0) * 1024)
-    assert r["source_hash"] == bench.kernel_hash("recurrence")
+    assert r["source_hash"] == bench.kernel_hash("recurrence", rec)
+    assert r["source_hash"] != bench.kernel_hash("recurrence")     # the two-half form's own file
     assert out["kernels"]["projection"]["fetch_kib"] == 20.0
 
 
@@ -90,8 +91,8 @@ def test_recorded_traffic_only_for_its_sources(monkeypatch):
     w = "lstm_bidir_s512_b64_i1024_h1024"
     with open(os.path.join(bench.ROOT, "profiles", f"{w}_traffic.json")) as f:
         rec = json.load(f)["kernels"]["recurrence"]
-    if rec["source_hash"] == bench.kernel_hash("recurrence"):
+    if rec["source_hash"] == bench.kernel_hash("recurrence", rec["name"]):
         assert bench.measured_traffic(w, "recurrence") == rec["traffic_bytes"]
     assert bench.measured_traffic("no_such_workload", "recurrence") is None
-    monkeypatch.setattr(bench, "kernel_hash", lambda stage: "0" * 16)
+    monkeypatch.setattr(bench, "kernel_hash", lambda stage, name="": "0" * 16)
     assert bench.measured_traffic(w, "recurrence") is None
