@@ -89,8 +89,9 @@ COPY_BYTES = 1 << 30
 
 
 def kernel_hash(stage, kernel_name=""):
-    """Hash of the sources of a stage's kernel (kernel_name: the measured
-    kernel's name, which adds the sources of its own form)."""
+    """Hash of the sources of a stage's kernel and the device compile flags
+    (kernel_name: the measured kernel's name, which adds the sources of its
+    own form)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "recurrent_nn_amd", "csrc")
@@ -101,6 +102,9 @@ def kernel_hash(stage, kernel_name=""):
     for n in names:
         with open(os.path.join(csrc, n), "rb") as f:
             h.update(n.encode() + b"\0" + f.read())
+    # the device compile flags change the code as much as the sources do
+    from recurrent_nn_amd import build as _build
+    h.update(" ".join(_build.HIP_FLAGS).encode())
     return h.hexdigest()[:16]
 
 

@@ -24,6 +24,9 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include")]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-ffp-contract=off",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # the flag and counter atomics are issued by one lane already:
+             # no lane-count reduction code in the step loops
+             "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
              "-Wno-unused-command-line-argument"]
 
 # The instantiation tables of the step loop: one source compiled once per

@@ -229,7 +229,9 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
     uint32_t hoff[2][P];                         // offset of the pair in an H plane (from drow)
     // XW element offsets fit 32 bits: the scratch limit keeps each
     // direction's projections under 2^30 floats
-    uint32_t xoff[2][P];
+    // (xbo: byte offset inside one step's rows of this direction, under 2^32)
+    uint32_t xoff[2][P], xbo[2][P];
+    const float *XWd = a.XW + (size_t)d * a.xw_steps * a.Bt * GH;
     size_t yoff[2][P];                           // offset of the pair's Y at step 0
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -247,6 +249,7 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
                 kc[h][k][e] = cst_u[e * a.U + u];
             hoff[h][k] = (uint32_t)(rl * Hp + gu);
             xoff[h][k] = (uint32_t)(xwd + (size_t)(row0 + rl) * GH + u);
+            xbo[h][k] = 4u * (uint32_t)((size_t)ub * a.G * a.U + (size_t)(row0 + rl) * GH + u);
             yoff[h][k] = a.layout == 0 ? ((size_t)d * a.Bt + b) * a.H + gu
                                        : ((size_t)b * a.S * a.D + d) * a.H + gu;
         }
@@ -334,22 +337,29 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
                     xw[k][g] = xw_next[h][k][g];
-            // (the next step's row is loaded whether or not the pair is still
-            // active there: an inactive pair's gate results are discarded,
-            // and the row lies inside the chunk's XW either way)
+            // The next step's XW row of each pair, issued inside the product
+            // right after the publish, so that neither the publish's wait for
+            // the H stores nor the flag poll's wait near the end of the
+            // product holds these memory reads (memory operations retire in
+            // issue order).  Issued at the last A prefetch instead, the poll's
+            // wait covered their latency: 10.2 against 10.05 us per step for
+            // the bidirectional LSTM of hidden size 1024, batch 64.  The row
+            // is loaded whether or not the pair is still active there (an
+            // inactive pair's gate results are discarded), by every lane (a
+            // lane without a pair reads the rows' first element) and at every
+            // step (the last one reloads its own row), with the gate's uniform
+            // base plus the pair's 32-bit byte offset as the address: no
+            // branch and little vector arithmetic inside the product.
             auto prefetch_xw = [&]() {
-                if (q + 1 < a.q_end) {
-                    const float *base = a.XW + (size_t)(q + 1 - a.j_base) * xstep;
+                const int qn = q + 1 < a.q_end ? q + 1 : q;
+                const char *base = (const char *)(XWd + (size_t)(qn - a.j_base) * xstep);
 #pragma unroll
-                    for (int k = 0; k < P; ++k)
-                        if (pk[h][k] >= 0) {
-                            const float *src = base + xoff[h][k];
+                for (int k = 0; k < P; ++k)
 #pragma unroll
-                            for (int g = 0; g < 4; ++g)
-                                if (g < G)
-                                    xw_next[h][k][g] = src[g * uc];
-                        }
-                }
+                    for (int g = 0; g < 4; ++g)
+                        if (g < G)
+                            xw_next[h][k][g] =
+                                *(const float *)(base + (size_t)g * uc * 4 + xbo[h][k]);
             };
 
             // ---- product over this wave's k range, this half's rows ---------
@@ -373,10 +383,11 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
                     fv = __hip_atomic_load(nflags + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             };
             product_res_hooked<MTH, NT, KBR, kPipePrefetch, KH, KP>(
-                acc, ring, a_src(pj, h), Hp, rr, prefetch_xw,
+                acc, ring, a_src(pj, h), Hp, rr, []() {},
                 [&]() {
                     const bool had = pend_h >= 0;
                     publish();
+                    prefetch_xw();
                     if (had)
                         RNN_STAMP(slot - 1, 5);   // the previous half's flag is out
                 },
