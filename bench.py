@@ -84,6 +84,9 @@ KERNEL_SOURCES = {
     "projection": ["proj_gemm.hip", "common.h"],
 }
 KERNEL_EXTRA_SOURCES = {"rec_pipe_kernel": ["recurrence_pipe.h"]}
+# the instantiation families a kernel is compiled in (their own device flags
+# count too)
+KERNEL_FAMILIES = {"rec_kernel": (0, 1, 2), "rec_pipe_kernel": (3,), "rec_fused_kernel": (4,)}
 KERNEL_NAMES = {"recurrence": "rec_", "projection": "proj_gemm"}
 COPY_BYTES = 1 << 30
 
@@ -105,6 +108,11 @@ def kernel_hash(stage, kernel_name=""):
     # the device compile flags change the code as much as the sources do
     from recurrent_nn_amd import build as _build
     h.update(" ".join(_build.HIP_FLAGS).encode())
+    for key, fams in KERNEL_FAMILIES.items():
+        if key in kernel_name:
+            for f in fams:
+                if _build.FAMILY_FLAGS.get(f):
+                    h.update(f"{f}:{' '.join(_build.FAMILY_FLAGS[f])}".encode())
     return h.hexdigest()[:16]
 
 

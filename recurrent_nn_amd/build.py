@@ -35,11 +35,19 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-ffp-contract=off",
 INST = "recurrence_inst.hip"
 INST_UNITS = [(fam, act) for fam in range(5) for act in range(5)]
 
+# Device flags of single kernel families.  The streamed step loops (families
+# 1 and 2) keep the matrix accumulators in ordinary vector registers: in the
+# default form the register allocator moved part of them between
+# accumulation registers at every back edge of the k loop (60 extra vector
+# instructions per 192 MFMAs with all row tiles of a 128-row block active).
+FAMILY_FLAGS = {1: ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                2: ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 # (source, extra flags, object name) of every translation unit: the .hip
 # files of csrc, the instantiation units, the HIP host code
 HIP_UNITS = ([(f, [], f + ".o") for f in sorted(os.listdir(CSRC))
               if f.endswith(".hip") and f != INST] +
-             [(INST, [f"-DRNN_FAMILY={fam}", f"-DRNN_ACT={act}"],
+             [(INST, [f"-DRNN_FAMILY={fam}", f"-DRNN_ACT={act}", *FAMILY_FLAGS.get(fam, [])],
                f"recurrence_inst_f{fam}_a{act}.o") for fam, act in INST_UNITS] +
              [("run.cpp", [], "run.cpp.o")])
 CXX_UNITS = [("plan.cpp", [], "plan.cpp.o")]

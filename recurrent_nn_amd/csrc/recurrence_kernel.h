@@ -252,13 +252,36 @@ __device__ __forceinline__ void product_stream(f4 (&acc)[MT][NT], const float *a
         if constexpr (MTA == 0) {
             mid();                                   // no active row: only the XW prefetch
         } else {
-            load(a0, b0, 0);
+            // (per-tile pointers advanced once per two blocks; the blocks'
+            // offsets from them are constants)
+            const float *ap[MTA > 0 ? MTA : 1], *bp[NT];
+#pragma unroll
+            for (int mt = 0; mt < MTA; ++mt)
+                ap[mt] = asrc + (size_t)mt * 16 * Hp;
+#pragma unroll
+            for (int nt = T0; nt < T1; ++nt)
+                bp[nt] = rfrag + (size_t)nt * 16 * Hp;
+            auto load_at = [&](auto &av, f4 (&bv)[NT], int off) {
+#pragma unroll
+                for (int mt = 0; mt < MTA; ++mt)
+                    av[mt] = *(const f4 *)(ap[mt] + off);
+#pragma unroll
+                for (int nt = T0; nt < T1; ++nt)
+                    bv[nt] = *(const f4 *)(bp[nt] + off);
+            };
+            load_at(a0, b0, 0);
             int kb = 0;
             for (; kb + 2 < KB; kb += 2) {
-                load(a1, b1, kb + 1);
+                load_at(a1, b1, 16);
                 mma(a0, b0);
-                load(a0, b0, kb + 2);
+                load_at(a0, b0, 32);
                 mma(a1, b1);
+#pragma unroll
+                for (int mt = 0; mt < MTA; ++mt)
+                    ap[mt] += 32;
+#pragma unroll
+                for (int nt = T0; nt < T1; ++nt)
+                    bp[nt] += 32;
             }
             if (KB - kb == 2) {                      // two blocks left
                 load(a1, b1, kb + 1);
@@ -748,26 +771,31 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
                 }
             } else if constexpr (PH == 1) {
                 static_assert(P % 2 == 0, "pairs are taken two at a time");
+                constexpr int NB = P % 4 == 0 ? 4 : 2;
 #pragma unroll 1
-                for (int i = 0; i < P; i += 2) {
+                for (int i = 0; i < P; i += NB) {
                     const int pi0 = tid + kThreads * i;
-                    if (npairs >= kThreads * (i + 2)) {
-                        const int pis[2] = {pi0, pi0 + kThreads};
-                        gates_n(std::integral_constant<int, 2>{}, pis, xw, F, Gf, Hf);
+                    if (npairs >= kThreads * (i + NB)) {
+                        int pis[NB];
+#pragma unroll
+                        for (int n = 0; n < NB; ++n)
+                            pis[n] = pi0 + kThreads * n;
+                        gates_n(std::integral_constant<int, NB>{}, pis, xw, F, Gf, Hf);
                     } else {
-                        if (pi0 < npairs)
-                            gates_n(std::integral_constant<int, 1>{}, &pi0, xw, F, Gf, Hf);
-                        const int pi1 = pi0 + kThreads;
-                        if (pi1 < npairs)
-                            gates_n(std::integral_constant<int, 1>{}, &pi1, xw + 1, F, Gf, Hf);
+#pragma unroll
+                        for (int n = 0; n < NB; ++n) {
+                            const int pin = pi0 + kThreads * n;
+                            if (pin < npairs)
+                                gates_n(std::integral_constant<int, 1>{}, &pin, xw + n, F, Gf, Hf);
+                        }
                     }
-                    if (npairs <= kThreads * (i + 2))
+                    if (npairs <= kThreads * (i + NB))
                         break;
 #pragma unroll
-                    for (int k = 0; k + 2 < P; ++k)
+                    for (int k = 0; k + NB < P; ++k)
 #pragma unroll
                         for (int g = 0; g < 4; ++g)
-                            xw[k][g] = xw[k + 2][g];
+                            xw[k][g] = xw[k + NB][g];
                 }
             } else {
 #pragma unroll 1

@@ -96,3 +96,16 @@ def test_recorded_traffic_only_for_its_sources(monkeypatch):
     assert bench.measured_traffic("no_such_workload", "recurrence") is None
     monkeypatch.setattr(bench, "kernel_hash", lambda stage, name="": "0" * 16)
     assert bench.measured_traffic(w, "recurrence") is None
+
+
+def test_family_flags_count_for_their_kernels_only(monkeypatch):
+    from recurrent_nn_amd import build
+    pipe = "void rnnamd::rec_pipe_kernel<2, 2, 16, 1, 1>(rnnamd::RecArgs)"
+    four = "void rnnamd::rec_kernel<8, 3, 0, 8, 0, 2, 4>(rnnamd::RecArgs)"
+    before = bench.kernel_hash("recurrence", pipe), bench.kernel_hash("recurrence", four)
+    flags = dict(build.FAMILY_FLAGS)
+    flags[2] = flags.get(2, []) + ["-mllvm", "-some-other-option"]
+    monkeypatch.setattr(build, "FAMILY_FLAGS", flags)
+    assert bench.kernel_hash("recurrence", pipe) == before[0]
+    assert bench.kernel_hash("recurrence", four) != before[1]
+
