@@ -30,8 +30,9 @@ namespace rnnamd {
 // k blocks ahead.  The first PD blocks are loaded by prime_ring beforehand
 // (so that their latency overlaps other work); `mid` runs right after the
 // last A prefetch, `hook` at the top of k block KH, before that block's
-// prefetch is issued, and `late` at the top of k block KP (after every A
-// prefetch when KP >= KBR - PD).
+// prefetch is issued, `late` at the top of k block KP (after every A
+// prefetch when KP >= KBR - PD) and `check` at the top of k block KC (none
+// for KC < 0).
 template <int MT, int KBR, int PD>
 __device__ __forceinline__ void prime_ring(f4 (&ring)[(PD < KBR ? PD : KBR) + 1][MT],
                                            const float *asrc, int Hp)
@@ -44,13 +45,13 @@ __device__ __forceinline__ void prime_ring(f4 (&ring)[(PD < KBR ? PD : KBR) + 1]
             ring[p][mt] = *(const f4 *)(asrc + (size_t)mt * 16 * Hp + p * 16);
 }
 
-template <int MT, int NT, int KBR, int PD, int KH, int KP, typename Mid, typename Hook,
-          typename Late>
+template <int MT, int NT, int KBR, int PD, int KH, int KP, int KC, typename Mid, typename Hook,
+          typename Late, typename Check>
 __device__ __forceinline__ void product_res_hooked(f4 (&acc)[MT][NT],
                                                    f4 (&ring)[(PD < KBR ? PD : KBR) + 1][MT],
                                                    const float *asrc, int Hp,
                                                    const f4 (&rr)[NT][KBR], Mid mid, Hook hook,
-                                                   Late late)
+                                                   Late late, Check check)
 {
     constexpr int D_ = PD < KBR ? PD : KBR;
     if constexpr (D_ >= KBR)
@@ -61,6 +62,8 @@ __device__ __forceinline__ void product_res_hooked(f4 (&acc)[MT][NT],
             hook();
         if (kb == KP)
             late();
+        if (kb == KC)
+            check();
         if (kb + D_ < KBR) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
@@ -383,12 +386,25 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
             const uint32_t *nflags = flags0 + (size_t)nh * a.NUB + wub_lo;
             const int nfl = wub_hi - wub_lo + 1;
             const bool need_wait = has_next && nq > a.q_begin && !dead;
-            uint32_t fv = 0xffffffffu;
+            // The load is issued by every lane (lanes past the last flag
+            // read the first one again) and its value compared one k block
+            // later, so that a block of MFMAs runs under its round trip
+            // (9.79 -> 9.53 us per step for the bidirectional LSTM of hidden
+            // size 1024; compared right after the load, or only after the
+            // product's partial-tile barrier, it was slower).
+            uint32_t fv = 0u;
+            bool fset = false;
             auto poll_next = [&]() {
-                if (EARLY && need_wait && nfl <= 64 && lane < nfl)
-                    fv = __hip_atomic_load(nflags + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (EARLY)
+                    fv = __hip_atomic_load(nflags + (lane < nfl ? lane : 0), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
             };
-            product_res_hooked<MTH, NT, KBR, kPipePrefetch, KH, KP>(
+            auto check_next = [&]() {
+                if (EARLY)
+                    fset = __all(lane >= nfl || fv >= (uint32_t)nq);
+            };
+            constexpr int KC = KP + 1 < KBR ? KP + 1 : -1;
+            product_res_hooked<MTH, NT, KBR, kPipePrefetch, KH, KP, KC>(
                 acc, ring, a_src(pj, h), Hp, rr, []() {},
                 [&]() {
                     const bool had = pend_h >= 0;
@@ -397,7 +413,9 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
                     if (had)
                         RNN_STAMP(slot - 1, 5);   // the previous half's flag is out
                 },
-                poll_next);
+                poll_next, check_next);
+            if constexpr (KC < 0)
+                check_next();
             RNN_STAMP(slot, 2);
             // partial tiles, column-major: a lane's four rows of a column are
             // contiguous (one 16-byte store per tile)
@@ -412,7 +430,7 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
             // if they were all set, load the next product's first k blocks now,
             // so that their latency overlaps this half's gate arithmetic;
             // otherwise wait for them only before that product
-            primed = !need_wait || (EARLY && nfl <= 64 && __all(fv >= (uint32_t)nq));
+            primed = !need_wait || (EARLY && nfl <= 64 && fset);
             asm volatile("" ::: "memory");
             if (has_next && primed)
                 prime_ring<MTH, KBR, kPipePrefetch>(ring, a_src(h == 0 ? pj : pj1, nh), Hp);
