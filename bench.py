@@ -91,10 +91,20 @@ KERNEL_NAMES = {"recurrence": "rec_", "projection": "proj_gemm"}
 COPY_BYTES = 1 << 30
 
 
+def _code_only(text):
+    """C++ source without its comments, trailing blanks and empty lines: an
+    edit of a comment does not make a recorded measurement stale."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def kernel_hash(stage, kernel_name=""):
-    """Hash of the sources of a stage's kernel and the device compile flags
-    (kernel_name: the measured kernel's name, which adds the sources of its
-    own form)."""
+    """Hash of the code (comments left out) of the sources of a stage's
+    kernel and the device compile flags (kernel_name: the measured kernel's
+    name, which adds the sources of its own form and the flags of the
+    families it is compiled in)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "recurrent_nn_amd", "csrc")
@@ -103,8 +113,8 @@ def kernel_hash(stage, kernel_name=""):
         if key in kernel_name:
             names += extra
     for n in names:
-        with open(os.path.join(csrc, n), "rb") as f:
-            h.update(n.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, n)) as f:
+            h.update(n.encode() + b"\0" + _code_only(f.read()).encode())
     # the device compile flags change the code as much as the sources do
     from recurrent_nn_amd import build as _build
     h.update(" ".join(_build.HIP_FLAGS).encode())

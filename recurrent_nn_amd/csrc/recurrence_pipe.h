@@ -116,10 +116,10 @@ __global__ void __launch_bounds__(256, 1) rec_pipe_kernel(RecArgs a)
     // at block 2 of 16 measured 2% faster than at block 8, at 0 slower)
     constexpr int KH = KBR >= 4 ? 2 : KBR / 2;
     // k block where the next product's flags are polled: after the publish,
-    // and one block after the last A prefetch is issued (the wave waits for
-    // the poll's load right away, so the later it goes the more flags are
-    // already set: at block 14 of 16 the step loop of a bidirectional LSTM
-    // of hidden size 1024, batch 64, took 9.76 us per step against 10.05 at
+    // and one block after the last A prefetch is issued (the later it goes,
+    // the more flags are already set: with the value compared right after
+    // the load, at block 14 of 16 the step loop of a bidirectional LSTM of
+    // hidden size 1024, batch 64, took 9.76 us per step against 10.05 at
     // block 13, and a hidden-1024 GRU 8.96 against 9.17; block 15 was the
     // same as 14)
     constexpr int KPF = KBR - (kPipePrefetch < KBR ? kPipePrefetch : KBR);

@@ -109,3 +109,11 @@ def test_family_flags_count_for_their_kernels_only(monkeypatch):
     assert bench.kernel_hash("recurrence", pipe) == before[0]
     assert bench.kernel_hash("recurrence", four) != before[1]
 
+
+
+def test_source_hash_ignores_comments():
+    a = "int f(int x) {\n    return x + 1;   // one more\n}\n"
+    b = "/* the successor */\nint f(int x) {\n\n    return x + 1;\n}\n"
+    c = "int f(int x) {\n    return x + 2;\n}\n"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
