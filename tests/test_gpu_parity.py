@@ -587,3 +587,26 @@ def test_long_two_half_run_matches_oracle():
         t = int(np.argwhere(bad)[0][0])
         raise AssertionError(f"first step differing: {t} (max abs there {err[t].max():.3e})")
     compare(c, gpu, ref, strict=True)
+
+
+# The two-half kernel's other operators and tiles over hundreds of steps:
+# the flag poll inside the product and the next step's XW rows loaded after
+# the publish, for GRU (three gates, one column tile), LSTM with lengths and
+# a 32-row batch tile, and a reverse RNN; every element is compared
+LONG_TWO_HALF = [
+    ("GRU", "forward", 512, 64, 256, 1024, {"linear_before_reset": 1}),
+    ("LSTM", "bidirectional", 384, 32, 256, 1024, {"with_lens": True}),
+    ("RNN", "reverse", 512, 64, 128, 1024, {}),
+]
+
+
+@pytest.mark.parametrize("k", range(len(LONG_TWO_HALF)))
+def test_long_two_half_runs_of_each_operator_match_oracle(k):
+    op, direction, S, Bt, I, H, kw = LONG_TWO_HALF[k]
+    c = workloads.random_case(op, direction, S, Bt, I, H, seed=4242, with_h0=True,
+                              with_c0=(op == "LSTM"), scale=1.0 / H ** 0.5, x_scale=0.5, **kw)
+    with ra.plan_for_case(c) as plan:
+        desc = plan.describe()
+    say(f"case {c.name}: {desc}")
+    assert "halves=2" in desc and "KB=16" in desc
+    compare(c, run_gpu(c), oracle_outputs(c), strict=True)
