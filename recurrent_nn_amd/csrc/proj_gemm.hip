@@ -459,13 +459,18 @@ __global__ void __launch_bounds__(256) proj_exact_kernel(ProjArgs a)
             gb[i] = load4k(true, rb_[i], k0 + sk);
         }
     };
+    // k-major tiles with the row index XOR-swizzled by 4 x ((k / 4) mod 8):
+    // the staging stores (eight k groups of a row per eight lanes) spread
+    // over all banks, and each thread's four consecutive rows stay one
+    // aligned 16-byte word for the reads
+    auto sw = [](int k) { return 4 * ((k >> 2) & 7); };
     auto sstore = [&]() {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                As[sk + e][sr + 32 * i] = ga[i][e];
-                Bs[sk + e][sr + 32 * i] = gb[i][e];
+                As[sk + e][(sr + 32 * i) ^ sw(sk + e)] = ga[i][e];
+                Bs[sk + e][(sr + 32 * i) ^ sw(sk + e)] = gb[i][e];
             }
     };
 
@@ -484,8 +489,8 @@ __global__ void __launch_bounds__(256) proj_exact_kernel(ProjArgs a)
         if (k0 + KC < a.K)
             gload(k0 + KC);
         for (int kk = 0; kk < kn; ++kk) {
-            const f4 av = *(const f4 *)&As[kk][4 * ty];
-            const f4 bv = *(const f4 *)&Bs[kk][4 * tx];
+            const f4 av = *(const f4 *)&As[kk][(4 * ty) ^ sw(kk)];
+            const f4 bv = *(const f4 *)&Bs[kk][(4 * tx) ^ sw(kk)];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
