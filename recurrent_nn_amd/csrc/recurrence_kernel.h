@@ -755,8 +755,10 @@ __global__ void __launch_bounds__(64 * NW, 1) rec_kernel(RecArgs a)
         };
 
         // Pairs tid + kThreads i.  Up to 2 pairs: one at a time, unrolled.  Up
-        // to 8 pairs, one phase: two at a time where every thread has both (a
-        // uniform test), in a loop that is not unrolled -- unrolled, the LDS
+        // to 8 pairs, one phase: four at a time (two when the count is not a
+        // multiple of four) where every thread has all of them (a uniform
+        // test; four measured 1% faster than two at 8 pairs per thread), in a
+        // loop that is not unrolled -- unrolled, the LDS
         // addresses of every pair are hoisted out of the step loop and spill
         // -- with the pairs' XW values moved down the array instead of
         // indexed at run time.  Up to 8 pairs, two phases (GRU,
