@@ -28,7 +28,8 @@ def _digest(outs):
 
 
 FUSED = [
-    # the C4 tile (64 rows, two column tiles, 16 k blocks per wave); I = 512:
+    # the LSTM benchmark workload's tile (64 rows, two column tiles, 16 k
+    # blocks per wave); I = 512:
     # the flag goes out inside the projection; peepholes, clip, lengths
     dict(op="LSTM", direction="bidirectional", S=9, Bt=64, I=512, H=1024, with_p=True, clip=0.9,
          with_lens=True),
@@ -82,7 +83,7 @@ def test_fused_projection_matches_separate_launch_bitwise_and_the_oracle(k):
 
 
 def test_long_fused_run_matches_oracle():
-    # the fused kernel with the C4 tile over 1024 steps (2048 hand-overs per
+    # the fused kernel with that tile over 1024 steps (2048 hand-overs per
     # workgroup, the flag from inside the projection); every element is
     # compared, and the first step that differs is named
     c = workloads.random_case("LSTM", "forward", 1024, 64, 512, 1024, seed=87, with_h0=True,
